@@ -1,0 +1,118 @@
+/*
+ * h3attn -- packed full attention for the MiniMax-H3 Omni-Transformer block on
+ * AMD Instinct MI355X (gfx950).  Plain C ABI, no C++ or torch types.
+ *
+ * The path: per-head Q/K RMSNorm -> partial three-axis MM-RoPE (both in
+ * h3attn_qk_prologue) -> full bidirectional softmax(Q K^T * scale) V
+ * (h3attn_forward), over one packed text + video + audio document.
+ *
+ * Definitions are those of the "MiniMax-H3 WS1/WS2 kernel roadmap" RFC:
+ *   section 2, Omni-Transformer fingerprint table (56 heads x 128, full
+ *   bidirectional self-attention, per-head Q/K RMSNorm with epsilon 1e-5,
+ *   three-axis (t, h, w) MM-RoPE with 16 frequencies per axis, theta 10000,
+ *   96 of 128 channels rotated and 32 passed through);
+ *   section 4, numerical contract (norm before RoPE, FP32 frequency
+ *   construction, non-causal unmasked attention over one document, fixed
+ *   reduction order, no split-KV or atomics, fail closed on unsupported input);
+ *   section 5, work items h3_qk_rmsnorm_d128, h3_mm_rope_3axis_partial and
+ *   h3_full_attention.
+ *
+ * Common conventions
+ *   - Tensors q, k, v, out are bfloat16 (raw 16-bit patterns), contiguous,
+ *     token-major [L][H][128]: element (l, h, c) sits at ((l*H + h)*128 + c).
+ *     Batch is not an argument: a batch is a replication axis, so callers
+ *     issue one call per document.
+ *   - All pointers are device memory owned by the caller.  The library
+ *     allocates nothing, keeps no state between calls, and only enqueues work
+ *     on `stream` (0 = the null stream): the calls return before the GPU
+ *     finishes, and the caller synchronises.
+ *   - Arguments are validated on the host before any launch; a rejected call
+ *     launches nothing and leaves every buffer untouched.  There is no
+ *     fallback path.  Device data is not inspected: non-finite inputs
+ *     propagate, and positions must satisfy |pos| <= 2^24 (exact in fp32).
+ *   - Results are deterministic: a fixed key order and one workgroup per
+ *     output row, independent of launch geometry, so repeated calls are
+ *     bit-identical.
+ */
+#ifndef H3ATTN_H
+#define H3ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3ATTN_ABI_VERSION 1
+#define H3ATTN_HEAD_DIM 128
+
+/* Status codes. */
+#define H3A_OK 0            /* success (work enqueued)                               */
+#define H3A_EINVAL 1        /* null pointer, L <= 0, H <= 0, misalignment, overlap,   */
+                            /* or a non-finite / non-positive scale                   */
+#define H3A_EUNSUPPORTED 2  /* geometry outside the supported range (L >= 2^31,       */
+                            /* grid or size overflow)                                 */
+#define H3A_EHIP 3          /* the HIP launch reported an error                       */
+
+/*
+ * Q/K prologue, in place: for every token l and head h,
+ *   q[l,h,:] <- RoPE_pos[l]( RMSNorm_gamma_q( q[l,h,:] ) )
+ *   k[l,h,:] <- RoPE_pos[l]( RMSNorm_gamma_k( k[l,h,:] ) )
+ * RMSNorm: y_c = x_c / sqrt(mean_c(x_c^2) + 1e-5) * gamma_c over the 128
+ * channels of one head, evaluated in fp32.
+ * MM-RoPE: with w_j = 10000^(-j/16) (j = 0..15, fp32) and angles
+ * phi_{16a+j} = pos[l,a] * w_j for axes a = t, h, w, channel c < 48 and its
+ * partner c + 48 rotate by phi_c:
+ *   out_c    = y_c * cos(phi_c) - y_{c+48} * sin(phi_c)
+ *   out_{c+48} = y_{c+48} * cos(phi_c) + y_c * sin(phi_c)
+ * and channels 96..127 pass through.  One round-to-nearest-even to bf16 at
+ * the end; accurate fp32 sine and cosine.
+ *
+ *   q, k     bf16 [L][H][128], read and rewritten in place; 16-byte aligned;
+ *            the two ranges must not overlap.
+ *   gamma_q, gamma_k  fp32 [128] RMSNorm weights, shared by all heads;
+ *            4-byte aligned.
+ *   pos_thw  int32 [L][3] per-token (t, h, w) positions; 4-byte aligned.
+ *   L        tokens in the packed document, 1 <= L < 2^31.
+ *   H        heads, >= 1.
+ */
+int h3attn_qk_prologue(void* q, void* k, const float* gamma_q, const float* gamma_k,
+                       const int32_t* pos_thw, int64_t L, int32_t H, hipStream_t stream);
+
+/*
+ * Full bidirectional attention, per head h, over all L tokens with no mask:
+ *   out[i,h,:] = sum_j softmax_j( scale * <q[i,h,:], k[j,h,:]> ) * v[j,h,:]
+ * S = Q K^T and P V on bf16 matrix cores with fp32 accumulation; online
+ * softmax in fp32 (P rounded to bf16 as the P V operand); the output is
+ * divided by the fp32 row sum and rounded to bf16 (round to nearest even).
+ *
+ *   q, k, v  bf16 [L][H][128] inputs (q and k normally come from
+ *            h3attn_qk_prologue; v is used as given); 16-byte aligned; they
+ *            may alias one another.
+ *   out      bf16 [L][H][128] output; 16-byte aligned; must not overlap q, k
+ *            or v.
+ *   L, H     as above.
+ *   scale    softmax scale, finite and > 0 (1/sqrt(128) for the H3 block).
+ */
+int h3attn_forward(const void* q, const void* k, const void* v, void* out, int64_t L,
+                   int32_t H, float scale, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* h3attn_strerror(int status);
+
+/*
+ * Detail of the last failed call on the calling thread (which argument was
+ * rejected, or the HIP error string); "" when the last call succeeded.
+ * The pointer stays valid until the next h3attn call on the same thread.
+ */
+const char* h3attn_last_error(void);
+
+/* H3ATTN_ABI_VERSION of the built library. */
+int h3attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3ATTN_H */

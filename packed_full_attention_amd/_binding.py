@@ -1,0 +1,129 @@
+"""ctypes binding of libh3attn (argument marshalling only).
+
+Every step of the path runs in the HIP kernels behind the C ABI; this module
+checks torch tensors (dtype, device, contiguity, shape), passes their device
+pointers and torch's current stream, and turns a non-zero status into an
+exception.  There is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libh3attn.so")
+HEAD_DIM = 128
+H3A_OK, H3A_EINVAL, H3A_EUNSUPPORTED, H3A_EHIP = 0, 1, 2, 3
+EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward", "h3attn_strerror",
+                    "h3attn_last_error", "h3attn_abi_version")
+
+_lock = threading.Lock()
+_lib: Optional[ctypes.CDLL] = None
+
+
+class H3AttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: status {status}: {message}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libh3attn.so and declare its signatures (raises if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path == LIB_PATH:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m packed_full_attention_amd.build` (there is no fallback path)")
+        lib = ctypes.CDLL(path)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        lib.h3attn_qk_prologue.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp]
+        lib.h3attn_qk_prologue.restype = ctypes.c_int
+        lib.h3attn_forward.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, vp]
+        lib.h3attn_forward.restype = ctypes.c_int
+        lib.h3attn_strerror.argtypes = [ctypes.c_int]
+        lib.h3attn_strerror.restype = ctypes.c_char_p
+        lib.h3attn_last_error.argtypes = []
+        lib.h3attn_last_error.restype = ctypes.c_char_p
+        lib.h3attn_abi_version.argtypes = []
+        lib.h3attn_abi_version.restype = ctypes.c_int
+        if path == LIB_PATH:
+            _lib = lib
+        return lib
+
+
+def _raise_on(lib, fn: str, status: int) -> None:
+    if status != H3A_OK:
+        detail = lib.h3attn_last_error().decode()
+        raise H3AttnError(fn, status, f"{lib.h3attn_strerror(status).decode()} ({detail})")
+
+
+def _check_tensor(name, t, dtype, shape, device=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _lh(q):
+    import torch
+    if not isinstance(q, torch.Tensor) or q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be a [L, H, {HEAD_DIM}] tensor")
+    return int(q.shape[0]), int(q.shape[1])
+
+
+def h3attn_qk_prologue(q, k, gamma_q, gamma_k, pos_thw) -> None:
+    """In-place Q/K RMSNorm + MM-RoPE on bf16 [L, H, 128] q and k (see include/h3attn.h)."""
+    import torch
+    L, H = _lh(q)
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, (L, H, HEAD_DIM))
+    _check_tensor("k", k, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    _check_tensor("gamma_q", gamma_q, torch.float32, (HEAD_DIM,), dev)
+    _check_tensor("gamma_k", gamma_k, torch.float32, (HEAD_DIM,), dev)
+    _check_tensor("pos_thw", pos_thw, torch.int32, (L, 3), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.h3attn_qk_prologue(q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(),
+                                    pos_thw.data_ptr(), L, H, stream)
+    _raise_on(lib, "h3attn_qk_prologue", st)
+
+
+def h3attn_forward(q, k, v, out=None, scale: Optional[float] = None):
+    """Full bidirectional attention on bf16 [L, H, 128]; returns out (see include/h3attn.h)."""
+    import torch
+    L, H = _lh(q)
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, (L, H, HEAD_DIM))
+    _check_tensor("k", k, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    _check_tensor("v", v, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.h3attn_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), L, H,
+                                float(scale), stream)
+    _raise_on(lib, "h3attn_forward", st)
+    return out
+
+
+def abi_version() -> int:
+    return int(load_library().h3attn_abi_version())

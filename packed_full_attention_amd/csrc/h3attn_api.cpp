@@ -1,0 +1,105 @@
+// C ABI of libh3attn: argument validation, then one kernel launch per call.
+//
+// Validation is synchronous, happens before any HIP call and rejects instead of
+// falling back (fail closed: "MiniMax-H3 WS1/WS2 kernel roadmap" RFC, section 4
+// item 9 and section 7 "Per-operator gate": empty, mis-shaped or unsupported
+// inputs fail clearly).  Device contents are never inspected.
+#include "h3attn.h"
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "h3attn_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256];
+
+int fail(int status, const char* fmt, const char* detail = nullptr) {
+  snprintf(g_last_error, sizeof g_last_error, fmt, detail ? detail : "");
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return H3A_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Do the byte ranges [a, a+na) and [b, b+nb) overlap?
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+constexpr int64_t kMaxThreadsPerGrid = (int64_t)1 << 32;  // work-items per grid dimension
+
+// Common shape checks; on success *bytes is the size of one [L][H][128] bf16 tensor.
+int check_shape(int64_t L, int32_t H, uint64_t* bytes) {
+  if (L <= 0) return fail(H3A_EINVAL, "L must be >= 1 (empty documents are rejected)%s");
+  if (H <= 0) return fail(H3A_EINVAL, "H must be >= 1%s");
+  if (L >= ((int64_t)1 << 31)) return fail(H3A_EUNSUPPORTED, "L must be < 2^31%s");
+  const __int128 elems = (__int128)L * H * H3ATTN_HEAD_DIM;
+  if (elems * 2 > ((__int128)1 << 62)) return fail(H3A_EUNSUPPORTED, "L*H*128 too large%s");
+  *bytes = (uint64_t)(elems * 2);
+  return H3A_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int h3attn_abi_version(void) { return H3ATTN_ABI_VERSION; }
+
+const char* h3attn_strerror(int status) {
+  switch (status) {
+    case H3A_OK: return "success";
+    case H3A_EINVAL: return "invalid argument";
+    case H3A_EUNSUPPORTED: return "unsupported geometry";
+    case H3A_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* h3attn_last_error(void) { return g_last_error; }
+
+int h3attn_qk_prologue(void* q, void* k, const float* gamma_q, const float* gamma_k,
+                       const int32_t* pos_thw, int64_t L, int32_t H, hipStream_t stream) {
+  if (!q || !k || !gamma_q || !gamma_k || !pos_thw)
+    return fail(H3A_EINVAL, "null pointer argument%s");
+  uint64_t bytes = 0;
+  if (int s = check_shape(L, H, &bytes)) return s;
+  if (!aligned(q, 16) || !aligned(k, 16)) return fail(H3A_EINVAL, "q and k must be 16-byte aligned%s");
+  if (!aligned(gamma_q, 4) || !aligned(gamma_k, 4) || !aligned(pos_thw, 4))
+    return fail(H3A_EINVAL, "gamma_q, gamma_k and pos_thw must be 4-byte aligned%s");
+  if (overlap(q, bytes, k, bytes)) return fail(H3A_EINVAL, "q and k overlap%s");
+  if (h3attn::prologue_grid_blocks(L) * 256 >= kMaxThreadsPerGrid)
+    return fail(H3A_EUNSUPPORTED, "prologue grid too large for L%s");
+  const hipError_t e = h3attn::launch_qk_prologue(static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
+                                                  gamma_q, gamma_k, pos_thw, L, H, stream);
+  if (e != hipSuccess) return fail(H3A_EHIP, "prologue launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int h3attn_forward(const void* q, const void* k, const void* v, void* out, int64_t L, int32_t H,
+                   float scale, hipStream_t stream) {
+  if (!q || !k || !v || !out) return fail(H3A_EINVAL, "null pointer argument%s");
+  uint64_t bytes = 0;
+  if (int s = check_shape(L, H, &bytes)) return s;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(H3A_EINVAL, "q, k, v and out must be 16-byte aligned%s");
+  if (!(isfinite(scale) && scale > 0.0f)) return fail(H3A_EINVAL, "scale must be finite and > 0%s");
+  if (overlap(out, bytes, q, bytes) || overlap(out, bytes, k, bytes) || overlap(out, bytes, v, bytes))
+    return fail(H3A_EINVAL, "out overlaps q, k or v%s");
+  if (h3attn::attention_grid_blocks(L, H) * 256 >= kMaxThreadsPerGrid)
+    return fail(H3A_EUNSUPPORTED, "attention grid too large for (L, H)%s");
+  const hipError_t e = h3attn::launch_attention_forward(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<uint16_t*>(out), L, H, scale, stream);
+  if (e != hipSuccess) return fail(H3A_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

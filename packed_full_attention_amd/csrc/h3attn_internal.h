@@ -1,0 +1,24 @@
+// Internal launch entry points shared by the C ABI layer and the kernel files.
+// Arguments are already validated by the caller (h3attn_api.cpp).
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace h3attn {
+
+// Enqueue the fused Q/K RMSNorm + MM-RoPE kernel (in place on q and k).
+hipError_t launch_qk_prologue(uint16_t* q, uint16_t* k, const float* gamma_q,
+                              const float* gamma_k, const int32_t* pos, int64_t L, int32_t H,
+                              hipStream_t stream);
+
+// Enqueue the flash-attention forward kernel.
+hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                    uint16_t* out, int64_t L, int32_t H, float scale,
+                                    hipStream_t stream);
+
+// Largest grid the forward launch accepts for (L, H); used by validation.
+int64_t attention_grid_blocks(int64_t L, int32_t H);
+int64_t prologue_grid_blocks(int64_t L);
+
+}  // namespace h3attn

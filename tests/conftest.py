@@ -25,3 +25,12 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # Name each GPU case on stderr, unbuffered, before it touches the device.
+    if "gpu" in request.keywords:
+        sys.__stderr__.write(f"[gpu-case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

@@ -1,0 +1,110 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments before any HIP call.
+
+Only calls that validation rejects are made here (with fake device addresses);
+nothing is ever launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from packed_full_attention_amd import _binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return b.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3attn_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(b.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.h3attn_abi_version() == 1
+
+
+def test_strerror_strings(lib):
+    assert lib.h3attn_strerror(0) == b"success"
+    assert lib.h3attn_strerror(1) == b"invalid argument"
+    assert lib.h3attn_strerror(2) == b"unsupported geometry"
+    assert lib.h3attn_strerror(3) == b"HIP launch error"
+    assert lib.h3attn_strerror(99) == b"unknown status"
+
+
+A = 0x7F0000000000            # fake, 256-byte aligned device addresses, far apart
+B = 0x7F1000000000
+C = 0x7F2000000000
+O = 0x7F3000000000
+G = 0x7F4000000000
+P = 0x7F5000000000
+
+
+def prologue(lib, q=A, k=B, gq=G, gk=G + 512, pos=P, L=160, H=4):
+    return lib.h3attn_qk_prologue(q, k, gq, gk, pos, L, H, None)
+
+
+def forward(lib, q=A, k=B, v=C, out=O, L=160, H=4, scale=0.08838834764831845):
+    return lib.h3attn_forward(q, k, v, out, L, H, scale, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), 1, "null"), (dict(k=None), 1, "null"), (dict(gq=None), 1, "null"),
+    (dict(gk=None), 1, "null"), (dict(pos=None), 1, "null"),
+    (dict(L=0), 1, "empty"), (dict(L=-5), 1, "L must"), (dict(H=0), 1, "H must"), (dict(H=-1), 1, "H must"),
+    (dict(q=A + 8), 1, "aligned"), (dict(k=B + 2), 1, "aligned"), (dict(gq=G + 2), 1, "aligned"),
+    (dict(pos=P + 1), 1, "aligned"),
+    (dict(k=A + 160 * 4 * 128 * 2 - 256), 1, "overlap"), (dict(q=B - 256), 1, "overlap"),
+    (dict(L=1 << 31), 2, "2^31"), (dict(L=(1 << 31) - 1, H=1 << 30), 2, "too large"),
+    (dict(L=(1 << 30), H=1, k=A + (1 << 42)), 2, "grid"),
+])
+def test_prologue_rejects(lib, kw, code, msg):
+    assert prologue(lib, **kw) == code
+    assert msg in lib.h3attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), 1, "null"), (dict(k=None), 1, "null"), (dict(v=None), 1, "null"), (dict(out=None), 1, "null"),
+    (dict(L=0), 1, "empty"), (dict(H=0), 1, "H must"),
+    (dict(v=C + 8), 1, "aligned"), (dict(out=O + 4), 1, "aligned"),
+    (dict(scale=0.0), 1, "scale"), (dict(scale=-1.0), 1, "scale"), (dict(scale=float("nan")), 1, "scale"),
+    (dict(scale=float("inf")), 1, "scale"),
+    (dict(out=A), 1, "overlap"), (dict(out=B + 1024), 1, "overlap"), (dict(out=C - 1024), 1, "overlap"),
+    (dict(L=1 << 31), 2, "2^31"),
+    (dict(L=(1 << 31) - 1, H=56, q=1 << 46, k=2 << 46, v=3 << 46, out=4 << 46), 2, "grid"),
+])
+def test_forward_rejects(lib, kw, code, msg):
+    assert forward(lib, **kw) == code
+    assert msg in lib.h3attn_last_error().decode()
+
+
+def test_binding_rejects_bad_tensors_on_cpu():
+    import torch
+    q = torch.zeros(8, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        b.h3attn_forward(q, q, q)
+    with pytest.raises(TypeError, match="bfloat16"):
+        b.h3attn_forward(q.float(), q, q)
+    with pytest.raises(ValueError, match=r"\[L, H, 128\]"):
+        b.h3attn_forward(torch.zeros(8, 2, 64, dtype=torch.bfloat16), q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        b.h3attn_qk_prologue(q, q.clone(), torch.ones(128), torch.ones(128),
+                             torch.zeros(8, 3, dtype=torch.int32))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="no fallback"):
+        b.load_library(str(tmp_path / "libh3attn.so"))
