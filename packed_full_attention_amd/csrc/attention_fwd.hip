@@ -11,17 +11,31 @@
 // does not depend on the grid or on the number of CUs.
 //
 // Work decomposition.  A 256-thread workgroup owns BM = 128 query rows of one
-// head; each of its 4 waves owns 32 of them.  The workgroup streams the keys in
-// tiles of BN = 64 through LDS (K row-major, V transposed) and every wave runs
-//   S^T = K_tile * Q^T        (v_mfma_f32_32x32x16_bf16, 2 x 8 per tile)
-//   online softmax on S^T     (fp32; exp2 with scale*log2(e) folded in)
-//   O^T += V_tile^T * P^T     (v_mfma_f32_32x32x16_bf16, 4 x 4 per tile)
+// head; each of its 4 waves owns 32 of them.  Keys stream through LDS in tiles
+// of BN = 64, double-buffered: while the waves compute on tile t, the DMA
+// loads of tile t+1 (global_load_lds_dwordx4, no VGPR staging) fill the other
+// buffer; one barrier per tile.  Per tile every wave runs
+//   S^T = K_tile * Q^T        (v_mfma_f32_32x32x16_bf16, 2 x 8)
+//   online softmax on S^T     (fp32; exp2 with scale*log2(e) folded into an FMA)
+//   O^T += V_tile^T * P^T     (v_mfma_f32_32x32x16_bf16, 4 x 4)
 // Computing the transposed score block makes each lane own one query column
 // (lane % 32) and 16 keys of every 32-key block, so the fp32 accumulators of
-// S^T convert in place to the bf16 B operand of the P*V product: no LDS round
-// trip for P, and the row statistics need one cross-half exchange (lane ^ 32).
-// The MFMA k-slot order of P^T is whatever the accumulator layout gives; V^T is
-// written to LDS with its key positions permuted to the same order.
+// S^T convert in place to the bf16 B operand of the P*V product (no LDS round
+// trip for P), and the row statistics need one cross-half exchange (lane ^ 32).
+//
+// LDS layout.  K and V tiles are both stored row-major (one 256-byte row per
+// key, sixteen 16-byte chunks) with chunk c of row r at physical chunk
+// c ^ swz(r), swz(r) = 2*(r & 3) | ((r >> 2) & 1).  This one swizzle makes both
+// read patterns conflict-free: the K operand (8 consecutive rows, one chunk)
+// and the transposed V operand, which is read with ds_read_b64_tr_b16 (each
+// 16-lane group addresses 4 consecutive keys x 32 bytes and receives, per lane,
+// 4 consecutive keys of one channel).
+//
+// Softmax rescaling is lazy: the running maximum m used as the exponent offset
+// only moves when a tile's maximum exceeds it by more than 8 (in log2 units), so
+// P <= 2^8 and the O rescale is skipped on almost every tile.  The final O / l
+// is unchanged by the choice of offset because l sums exactly the bf16 P values
+// that enter the P*V product.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,42 +46,150 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 
 constexpr int kD = 128;
-constexpr int kBM = 128;               // query rows per workgroup
-constexpr int kBN = 64;                // keys per tile
+constexpr int kBM = 128;                 // query rows per workgroup
+constexpr int kBN = 64;                  // keys per tile
 constexpr int kThreads = 256;
-constexpr int kKPitch = kD + 8;        // bf16 per K row in LDS (272 B: conflict-free 16 B reads)
-constexpr int kVPitch = kBN + 8;       // bf16 per V^T row in LDS (144 B)
+constexpr int kTileBytes = kBN * kD * 2; // 16 KiB per K or V tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x2_t r;
   r[0] = (__bf16)a;
   r[1] = (__bf16)b;
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Key chunk (4 keys) -> LDS position chunk inside each 16-key group.  The
-// accumulator of S^T gives lane-half g the keys {4g..4g+3, 8+4g..8+4g+3} of a
-// 16-key step; storing key chunks in the order 0, 2, 1, 3 puts exactly those
-// 8 keys in LDS positions 8g..8g+7, one 16-byte read.
-__device__ __forceinline__ int vt_position(int key_in_tile) {
-  const int chunk = (key_in_tile >> 2) & 3;
-  const int pchunk = (chunk == 1) ? 2 : (chunk == 2) ? 1 : chunk;
-  return (key_in_tile & ~15) | (pchunk << 2) | (key_in_tile & 3);
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Byte offset of (row, channel) in a swizzled tile; channel % 4 == 0.
+__device__ __forceinline__ int tile_offset(int row, int ch) {
+  return row * (kD * 2) + ((((ch >> 3) ^ swz(row))) << 4) + ((ch & 7) << 1);
 }
 
-__global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
+// DMA one 64-key tile of a [L][H][128] tensor into a swizzled LDS tile.  Each
+// wave writes four contiguous 1 KiB pieces (64 lanes x 16 B, lane-ordered);
+// a lane fetches the global chunk that belongs at its slot.  Rows past the end
+// of the document re-read row L-1 (finite values; their scores are masked and
+// their probabilities are zero).
+__device__ __forceinline__ void tile_dma(const uint16_t* __restrict__ head_base, int64_t tok_stride,
+                                         int kbase, int L, lds_char* tile, int wave, int lane) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int piece = it * 4 + wave;            // 1 KiB piece = 4 rows
+    const int slot = piece * 64 + lane;         // 16-byte slot in the tile
+    const int r = slot >> 4;
+    const int c = (slot & 15) ^ swz(r);
+    const int key = min(kbase + r, L - 1);
+    const uint16_t* g = head_base + (int64_t)key * tok_stride + 8 * c;
+    __builtin_amdgcn_global_load_lds(g, tile + piece * 1024, 16, 0, 0);
+  }
+}
+
+// One tile: S^T, online softmax, O^T += V^T P^T.  kt/vt are the tile's LDS buffers.
+__device__ __forceinline__ void tile_step(const lds_char* kt, const lds_char* vt, const bf16x8_t (&qf)[8],
+                                          f32x16_t (&o)[4], float& m_run, float& l_run, int kbase,
+                                          int L, float c, int col, int g, int lane) {
+  // S^T[key][query] for the two 32-key blocks of the tile.
+  f32x16_t s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    s[kb] = f32x16_t{};
+    const int row = 32 * kb + col;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t a = *(const lds_bf16x8*)(kt + tile_offset(row, 16 * ks + 8 * g));
+      s[kb] = mfma32(a, qf[ks], s[kb]);
+    }
+  }
+  if (kbase + kBN > L) {  // keys past the end of the document do not exist
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          if (kbase + 32 * kb + 8 * r + 4 * g + qq >= L) s[kb][4 * r + qq] = -INFINITY;
+  }
+
+  // Tile maximum of this lane's query over both lane-halves.
+  float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s[0][e], s[1][e]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // Move the exponent offset only when the tile would push P above 2^8.  Both
+  // lane-halves of a query see the same mx and m_run, so they decide alike.
+  const bool need = (mx - m_run) * c > kRescaleThreshold;
+  if (__any(need)) {
+    const float m_new = need ? mx : m_run;
+    const float alpha = exp2f((m_run - m_new) * c);  // m_run = -inf on the first tile -> 0
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] *= alpha;
+    m_run = m_new;
+  }
+  // P = 2^(s*c - m*c), rounded to bf16 for the P*V product.  The row sum adds
+  // the same rounded values (v_dot2_f32_bf16 against (1, 1)), so the output is
+  // an exact convex combination of V rows with the weights the MFMA used.
+  const float mc = m_run * c;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x8_t pf[4];
+  float psum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      bf16x2_t pr;
+      pr[0] = (__bf16)exp2f(fmaf(s[kb][e], c, -mc));
+      pr[1] = (__bf16)exp2f(fmaf(s[kb][e + 1], c, -mc));
+      psum[e >> 2 & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum[e >> 2 & 3], false);
+      pf[2 * kb + (e >> 3)][e & 7] = pr[0];
+      pf[2 * kb + (e >> 3)][(e & 7) + 1] = pr[1];
+    }
+  l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+
+  // O^T[d][query] += V^T[d][keys] * P^T[keys][query].  The A operand for d-block
+  // dblk and 16-key step st comes from two transposed reads: lane l (group
+  // G = l >> 4, index i = l & 15) addresses key 16*st + 4*(G >> 1) + (i >> 2)
+  // (+8 for the second read) at channel 32*dblk + 16*(G & 1) + 4*(i & 3), and
+  // receives keys {16 st + 4g + e} and {16 st + 8 + 4g + e} of channel
+  // 32*dblk + (l % 32) -- the same key order as the P^T accumulator slots.
+  const int G = lane >> 4, i = lane & 15;
+  const int key_a = 4 * (G >> 1) + (i >> 2);
+  const int ch = 16 * (G & 1) + 4 * (i & 3);
+#pragma unroll
+  for (int dblk = 0; dblk < 4; ++dblk) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vt + tile_offset(16 * st + key_a, 32 * dblk + ch)));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vt + tile_offset(16 * st + 8 + key_a, 32 * dblk + ch)));
+      typedef short i16x8_t __attribute__((ext_vector_type(8)));
+      const i16x8_t a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[dblk] = mfma32(__builtin_bit_cast(bf16x8_t, a16), pf[st], o[dblk]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, int L, int H, float scale_log2e, int n_qtiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBN * kKPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kD * kVPitch];
+  __shared__ __attribute__((aligned(1024))) char k_lds0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[kTileBytes];
 
   // Workgroups are dispatched round-robin over the 8 XCDs (block b -> XCD b%8).
   // Renumber so each XCD receives a contiguous run of (head, q-tile) work:
@@ -80,16 +202,22 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   const int qtile = logical - head * n_qtiles;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, g = lane >> 5;
   const int64_t tok_stride = (int64_t)H * kD;  // elements between consecutive tokens
-  const int64_t head_off = (int64_t)head * kD;
+  const uint16_t* kh = k + (int64_t)head * kD;
+  const uint16_t* vh = v + (int64_t)head * kD;
+
+  const int n_tiles = (L + kBN - 1) / kBN;
+  tile_dma(kh, tok_stride, 0, L, (lds_char*)k_lds0, wave, lane);
+  tile_dma(vh, tok_stride, 0, L, (lds_char*)v_lds0, wave, lane);
 
   // Q^T operand: lane holds Q[row][16ks + 8g .. +7] for its query row.
   const int qrow = qtile * kBM + wave * 32 + col;
   bf16x8_t qf[8];
   if (qrow < L) {
-    const uint16_t* p = q + (int64_t)qrow * tok_stride + head_off + 8 * g;
+    const uint16_t* p = q + (int64_t)qrow * tok_stride + (int64_t)head * kD + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(p + 16 * ks);
   } else {
@@ -100,114 +228,33 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   f32x16_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
-  float m_run = -INFINITY;  // running max of raw scores for this lane's query
-  float l_run = 0.f;        // this lane-half's partial running sum
+  float m_run = -INFINITY;  // exponent offset (raw score units) for this lane's query
+  float l_run = 0.f;        // this lane-half's partial sum of P
+  __syncthreads();          // tile 0 is in LDS
 
-  // Cooperative tile loaders.
-  // K: 64 keys x 16 sixteen-byte chunks; thread handles chunks tid + 256*it.
-  // V: thread handles keys 4*kq..4*kq+3 of d-chunk dc (8 channels); kq varies
-  //    fastest across lanes so a wave's transposed LDS writes hit distinct banks.
-  const int v_kq = tid & 15, v_dc = tid >> 4;
-  const int v_pos = vt_position(4 * v_kq);
-
-  const int n_tiles = (L + kBN - 1) / kBN;
-  for (int t = 0; t < n_tiles; ++t) {
-    const int kbase = t * kBN;
-    __syncthreads();  // all waves are done reading the previous tile
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = it * kThreads + tid;
-      const int key = idx >> 4, dc = idx & 15;
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (kbase + key < L)
-        val = *reinterpret_cast<const uint4*>(k + (int64_t)(kbase + key) * tok_stride + head_off + 8 * dc);
-      *reinterpret_cast<uint4*>(k_lds + key * kKPitch + 8 * dc) = val;
+  for (int t = 0; t < n_tiles; t += 2) {
+    if (t + 1 < n_tiles) {
+      tile_dma(kh, tok_stride, (t + 1) * kBN, L, (lds_char*)k_lds1, wave, lane);
+      tile_dma(vh, tok_stride, (t + 1) * kBN, L, (lds_char*)v_lds1, wave, lane);
     }
-    {
-      uint4 vv[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int key = kbase + 4 * v_kq + m;
-        vv[m] = make_uint4(0u, 0u, 0u, 0u);
-        if (key < L)
-          vv[m] = *reinterpret_cast<const uint4*>(v + (int64_t)key * tok_stride + head_off + 8 * v_dc);
-      }
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vv[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vv[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vv[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vv[3]);
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const int sh = (d & 1) * 16;
-        const uint32_t e0 = (w0[d >> 1] >> sh) & 0xffffu, e1 = (w1[d >> 1] >> sh) & 0xffffu;
-        const uint32_t e2 = (w2[d >> 1] >> sh) & 0xffffu, e3 = (w3[d >> 1] >> sh) & 0xffffu;
-        *reinterpret_cast<uint2*>(vt_lds + (8 * v_dc + d) * kVPitch + v_pos) =
-            make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-      }
+    tile_step((const lds_char*)k_lds0, (const lds_char*)v_lds0, qf, o, m_run, l_run, t * kBN, L,
+              scale_log2e, col, g, lane);
+    __syncthreads();  // tile t+1 landed; every wave is done with buffer 0
+    if (t + 1 >= n_tiles) break;
+    if (t + 2 < n_tiles) {
+      tile_dma(kh, tok_stride, (t + 2) * kBN, L, (lds_char*)k_lds0, wave, lane);
+      tile_dma(vh, tok_stride, (t + 2) * kBN, L, (lds_char*)v_lds0, wave, lane);
     }
-    __syncthreads();
-
-    // S^T[key][query] for the two 32-key blocks of the tile.
-    f32x16_t s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16_t{};
-      const uint16_t* kr = k_lds + (32 * kb + col) * kKPitch + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8_t*>(kr + 16 * ks), qf[ks], s[kb]);
-    }
-    // Keys past the end of the document do not exist.
-    if (kbase + kBN > L) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq)
-            if (kbase + 32 * kb + 8 * r + 4 * g + qq >= L) s[kb][4 * r + qq] = -INFINITY;
-    }
-
-    // Online softmax for this lane's query.
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f((m_run - m_new) * scale_log2e);
-    const float mc = m_new * scale_log2e;
-    float psum = 0.f;
-    bf16x8_t pf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(fmaf(s[kb][e], scale_log2e, -mc));
-        psum += p;
-        pf[2 * kb + (e >> 3)][e & 7] = (__bf16)p;
-      }
-    l_run = fmaf(l_run, alpha, psum);
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] *= alpha;
-
-    // O^T[d][query] += V^T[d][keys] * P^T[keys][query]
-#pragma unroll
-    for (int dblk = 0; dblk < 4; ++dblk) {
-      const uint16_t* vr = vt_lds + (32 * dblk + col) * kVPitch + 8 * g;
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        o[dblk] = mfma32(*reinterpret_cast<const bf16x8_t*>(vr + 16 * st), pf[st], o[dblk]);
-    }
+    tile_step((const lds_char*)k_lds1, (const lds_char*)v_lds1, qf, o, m_run, l_run, (t + 1) * kBN, L,
+              scale_log2e, col, g, lane);
+    __syncthreads();  // tile t+2 landed; every wave is done with buffer 1
   }
 
   // Epilogue: full row sum = both lane-halves; O / l -> bf16.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv_l = 1.0f / l_tot;
   if (qrow < L) {
-    uint16_t* po = out + (int64_t)qrow * tok_stride + head_off;
+    uint16_t* po = out + (int64_t)qrow * tok_stride + (int64_t)head * kD;
 #pragma unroll
     for (int dblk = 0; dblk < 4; ++dblk)
 #pragma unroll
