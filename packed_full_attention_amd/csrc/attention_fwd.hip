@@ -80,40 +80,51 @@ __device__ __forceinline__ int tile_offset(int row, int ch) {
 
 // DMA one 64-key tile of a [L][H][128] tensor into a swizzled LDS tile.  Each
 // wave writes four contiguous 1 KiB pieces (64 lanes x 16 B, lane-ordered);
-// a lane fetches the global chunk that belongs at its slot.  Rows past the end
-// of the document re-read row L-1 (finite values; their scores are masked and
-// their probabilities are zero).
-__device__ __forceinline__ void tile_dma(const uint16_t* __restrict__ head_base, int64_t tok_stride,
-                                         int kbase, int L, lds_char* tile, int wave, int lane) {
+// lane `lane` of piece p fetches the global chunk that belongs at its slot.
+// The tile base is wave-uniform and each lane adds a fixed 32-bit byte offset
+// (row * token stride + chunk), so per tile only the scalar base moves.
+struct DmaOffsets {
+  uint32_t off[4];
+};
+
+__device__ __forceinline__ DmaOffsets dma_offsets(int64_t tok_stride, int wave, int lane, int max_row) {
+  DmaOffsets d;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int piece = it * 4 + wave;            // 1 KiB piece = 4 rows
-    const int slot = piece * 64 + lane;         // 16-byte slot in the tile
+    const int slot = (it * 4 + wave) * 64 + lane;  // 16-byte slot in the tile
     const int r = slot >> 4;
     const int c = (slot & 15) ^ swz(r);
-    const int key = min(kbase + r, L - 1);
-    const uint16_t* g = head_base + (int64_t)key * tok_stride + 8 * c;
-    __builtin_amdgcn_global_load_lds(g, tile + piece * 1024, 16, 0, 0);
+    // Rows past the end of the document re-read the last row (finite values;
+    // their scores are masked and their probabilities are zero).
+    d.off[it] = (uint32_t)(((int64_t)min(r, max_row) * tok_stride + 8 * c) * 2);
   }
+  return d;
+}
+
+__device__ __forceinline__ void tile_dma(const char* tile_base, const DmaOffsets& d, lds_char* tile,
+                                         int wave) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+    __builtin_amdgcn_global_load_lds(tile_base + d.off[it], tile + (it * 4 + wave) * 1024, 16, 0, 0);
 }
 
 // One tile: S^T, online softmax, O^T += V^T P^T.  kt/vt are the tile's LDS buffers.
+template <bool kTail>
 __device__ __forceinline__ void tile_step(const lds_char* kt, const lds_char* vt, const bf16x8_t (&qf)[8],
                                           f32x16_t (&o)[4], float& m_run, float& l_run, int kbase,
                                           int L, float c, int col, int g, int lane) {
-  // S^T[key][query] for the two 32-key blocks of the tile.
-  f32x16_t s[2];
+  // S^T[key][query] for the two 32-key blocks of the tile; the two accumulation
+  // chains are interleaved so consecutive MFMAs are independent.
+  f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    s[kb] = f32x16_t{};
-    const int row = 32 * kb + col;
+  for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8_t a = *(const lds_bf16x8*)(kt + tile_offset(row, 16 * ks + 8 * g));
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8_t a = *(const lds_bf16x8*)(kt + tile_offset(32 * kb + col, 16 * ks + 8 * g));
       s[kb] = mfma32(a, qf[ks], s[kb]);
     }
   }
-  if (kbase + kBN > L) {  // keys past the end of the document do not exist
+  if (kTail) {  // keys past the end of the document do not exist
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -133,7 +144,7 @@ __device__ __forceinline__ void tile_step(const lds_char* kt, const lds_char* vt
   const bool need = (mx - m_run) * c > kRescaleThreshold;
   if (__any(need)) {
     const float m_new = need ? mx : m_run;
-    const float alpha = exp2f((m_run - m_new) * c);  // m_run = -inf on the first tile -> 0
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);  // m_run = -inf on the first tile -> 0
     l_run *= alpha;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] *= alpha;
@@ -151,8 +162,8 @@ __device__ __forceinline__ void tile_step(const lds_char* kt, const lds_char* vt
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
       bf16x2_t pr;
-      pr[0] = (__bf16)exp2f(fmaf(s[kb][e], c, -mc));
-      pr[1] = (__bf16)exp2f(fmaf(s[kb][e + 1], c, -mc));
+      pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][e], c, -mc));
+      pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][e + 1], c, -mc));
       psum[e >> 2 & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum[e >> 2 & 3], false);
       pf[2 * kb + (e >> 3)][e & 7] = pr[0];
       pf[2 * kb + (e >> 3)][(e & 7) + 1] = pr[1];
@@ -169,9 +180,9 @@ __device__ __forceinline__ void tile_step(const lds_char* kt, const lds_char* vt
   const int key_a = 4 * (G >> 1) + (i >> 2);
   const int ch = 16 * (G & 1) + 4 * (i & 3);
 #pragma unroll
-  for (int dblk = 0; dblk < 4; ++dblk) {
+  for (int st = 0; st < 4; ++st) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int dblk = 0; dblk < 4; ++dblk) {
       const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_i16x4*)(vt + tile_offset(16 * st + key_a, 32 * dblk + ch)));
       const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -209,9 +220,19 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
   const uint16_t* kh = k + (int64_t)head * kD;
   const uint16_t* vh = v + (int64_t)head * kD;
 
-  const int n_tiles = (L + kBN - 1) / kBN;
-  tile_dma(kh, tok_stride, 0, L, (lds_char*)k_lds0, wave, lane);
-  tile_dma(vh, tok_stride, 0, L, (lds_char*)v_lds0, wave, lane);
+  const int n_full = L / kBN;                 // tiles with 64 real keys
+  const int n_tiles = (L + kBN - 1) / kBN;    // plus one partial tile if L % 64 != 0
+  const int64_t tile_stride_bytes = (int64_t)kBN * tok_stride * 2;
+  const char* kbase_ptr = reinterpret_cast<const char*>(kh);
+  const char* vbase_ptr = reinterpret_cast<const char*>(vh);
+  const DmaOffsets dma_full = dma_offsets(tok_stride, wave, lane, kBN - 1);
+  const DmaOffsets dma_tail = dma_offsets(tok_stride, wave, lane, (L - 1) % kBN);
+  auto dma = [&](int t, lds_char* kt, lds_char* vt) {
+    const DmaOffsets& d = (t < n_full) ? dma_full : dma_tail;
+    tile_dma(kbase_ptr + t * tile_stride_bytes, d, kt, wave);
+    tile_dma(vbase_ptr + t * tile_stride_bytes, d, vt, wave);
+  };
+  dma(0, (lds_char*)k_lds0, (lds_char*)v_lds0);
 
   // Q^T operand: lane holds Q[row][16ks + 8g .. +7] for its query row.
   const int qrow = qtile * kBM + wave * 32 + col;
@@ -230,24 +251,32 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
   for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
   float m_run = -INFINITY;  // exponent offset (raw score units) for this lane's query
   float l_run = 0.f;        // this lane-half's partial sum of P
+  auto full_step = [&](int t, const lds_char* kt, const lds_char* vt) {
+    tile_step<false>(kt, vt, qf, o, m_run, l_run, t * kBN, L, scale_log2e, col, g, lane);
+  };
   __syncthreads();          // tile 0 is in LDS
 
-  for (int t = 0; t < n_tiles; t += 2) {
-    if (t + 1 < n_tiles) {
-      tile_dma(kh, tok_stride, (t + 1) * kBN, L, (lds_char*)k_lds1, wave, lane);
-      tile_dma(vh, tok_stride, (t + 1) * kBN, L, (lds_char*)v_lds1, wave, lane);
-    }
-    tile_step((const lds_char*)k_lds0, (const lds_char*)v_lds0, qf, o, m_run, l_run, t * kBN, L,
-              scale_log2e, col, g, lane);
+  // Full tiles, two per trip so each buffer is named statically; the loop body
+  // is one straight path.  The partial tile (if L % 64 != 0) is peeled below.
+  int t = 0;
+  for (; t + 1 < n_full; t += 2) {
+    dma(t + 1, (lds_char*)k_lds1, (lds_char*)v_lds1);
+    full_step(t, (const lds_char*)k_lds0, (const lds_char*)v_lds0);
     __syncthreads();  // tile t+1 landed; every wave is done with buffer 0
-    if (t + 1 >= n_tiles) break;
-    if (t + 2 < n_tiles) {
-      tile_dma(kh, tok_stride, (t + 2) * kBN, L, (lds_char*)k_lds0, wave, lane);
-      tile_dma(vh, tok_stride, (t + 2) * kBN, L, (lds_char*)v_lds0, wave, lane);
-    }
-    tile_step((const lds_char*)k_lds1, (const lds_char*)v_lds1, qf, o, m_run, l_run, (t + 1) * kBN, L,
-              scale_log2e, col, g, lane);
+    if (t + 2 < n_tiles) dma(t + 2, (lds_char*)k_lds0, (lds_char*)v_lds0);
+    full_step(t + 1, (const lds_char*)k_lds1, (const lds_char*)v_lds1);
     __syncthreads();  // tile t+2 landed; every wave is done with buffer 1
+  }
+  if (t < n_full) {  // odd number of full tiles: the last one sits in buffer 0
+    if (t + 1 < n_tiles) dma(t + 1, (lds_char*)k_lds1, (lds_char*)v_lds1);
+    full_step(t, (const lds_char*)k_lds0, (const lds_char*)v_lds0);
+    __syncthreads();
+    ++t;
+  }
+  if (t < n_tiles) {  // the partial tile, in buffer t % 2
+    const lds_char* kt = (t & 1) ? (const lds_char*)k_lds1 : (const lds_char*)k_lds0;
+    const lds_char* vt = (t & 1) ? (const lds_char*)v_lds1 : (const lds_char*)v_lds0;
+    tile_step<true>(kt, vt, qf, o, m_run, l_run, t * kBN, L, scale_log2e, col, g, lane);
   }
 
   // Epilogue: full row sum = both lane-halves; O / l -> bf16.
