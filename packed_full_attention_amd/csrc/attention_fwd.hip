@@ -25,11 +25,14 @@
 //
 // LDS layout.  K and V tiles are both stored row-major (one 256-byte row per
 // key, sixteen 16-byte chunks) with chunk c of row r at physical chunk
-// c ^ swz(r), swz(r) = 2*(r & 3) | ((r >> 2) & 1).  This one swizzle makes both
-// read patterns conflict-free: the K operand (8 consecutive rows, one chunk)
-// and the transposed V operand, which is read with ds_read_b64_tr_b16 (each
-// 16-lane group addresses 4 consecutive keys x 32 bytes and receives, per lane,
-// 4 consecutive keys of one channel).
+// c ^ swz(r), swz(r) = 4*(r & 3) + ((r >> 2) & 3).  The LDS has 64 four-byte
+// banks (one 256-byte row) and serves 16 lanes of a 16-byte read, or 32 lanes
+// of an 8-byte read, per cycle.  swz takes 16 distinct values over any 16
+// consecutive rows, so the K operand read (16 rows, one chunk) is
+// conflict-free; and for 4 consecutive rows its top two bits are distinct, so
+// the transposed V read (ds_read_b64_tr_b16: 32 lanes = 4 consecutive keys x
+// 4 aligned chunks; each lane receives 4 consecutive keys of one channel) is
+// conflict-free too.  Both were checked with the SQ_LDS_BANK_CONFLICT counter.
 //
 // Softmax rescaling is lazy: the running maximum m used as the exponent offset
 // only moves when a tile's maximum exceeds it by more than 8 (in log2 units), so
@@ -71,7 +74,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 // Byte offset of (row, channel) in a swizzled tile; channel % 4 == 0.
 __device__ __forceinline__ int tile_offset(int row, int ch) {
