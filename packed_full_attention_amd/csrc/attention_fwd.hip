@@ -11,34 +11,47 @@
 // does not depend on the grid or on the number of CUs.
 //
 // Work decomposition.  A 256-thread workgroup owns BM = 128 query rows of one
-// head; each of its 4 waves owns 32 of them.  Keys stream through LDS in tiles
-// of BN = 64, double-buffered: while the waves compute on tile t, the DMA
-// loads of tile t+1 (global_load_lds_dwordx4, no VGPR staging) fill the other
-// buffer; one barrier per tile.  Per tile every wave runs
+// head; each of its 4 waves owns 32 of them, and two workgroups share a CU (two
+// waves per SIMD).  Keys stream through LDS in tiles of BN = 64.  Per tile a
+// wave computes
 //   S^T = K_tile * Q^T        (v_mfma_f32_32x32x16_bf16, 2 x 8)
 //   online softmax on S^T     (fp32; exp2 with scale*log2(e) folded into an FMA)
 //   O^T += V_tile^T * P^T     (v_mfma_f32_32x32x16_bf16, 4 x 4)
 // Computing the transposed score block makes each lane own one query column
 // (lane % 32) and 16 keys of every 32-key block, so the fp32 accumulators of
 // S^T convert in place to the bf16 B operand of the P*V product (no LDS round
-// trip for P), and the row statistics need one cross-half exchange (lane ^ 32).
+// trip for P), and the row statistics need one cross-half exchange
+// (v_permlane32_swap, no LDS).
 //
-// LDS layout.  K and V tiles are both stored row-major (one 256-byte row per
-// key, sixteen 16-byte chunks) with chunk c of row r at physical chunk
-// c ^ swz(r), swz(r) = 4*(r & 3) + ((r >> 2) & 3).  The LDS has 64 four-byte
-// banks (one 256-byte row) and serves 16 lanes of a 16-byte read, or 32 lanes
-// of an 8-byte read, per cycle.  swz takes 16 distinct values over any 16
-// consecutive rows, so the K operand read (16 rows, one chunk) is
-// conflict-free; and for 4 consecutive rows its top two bits are distinct, so
-// the transposed V read (ds_read_b64_tr_b16: 32 lanes = 4 consecutive keys x
-// 4 aligned chunks; each lane receives 4 consecutive keys of one channel) is
-// conflict-free too.  Both were checked with the SQ_LDS_BANK_CONFLICT counter.
+// Software pipeline.  The score block of the next tile is computed while the
+// VALU works on the softmax of the current one:
+//   iteration t:  S(t+1) = K(t+1) Q^T   (matrix cores)
+//                 softmax of S(t)        (VALU, independent of S(t+1))
+//                 O += V(t)^T P(t)^T     (matrix cores)
+// so every wave has MFMA and VALU work in flight together, on top of the
+// overlap between the two waves that share a SIMD.
 //
-// Softmax rescaling is lazy: the running maximum m used as the exponent offset
-// only moves when a tile's maximum exceeds it by more than 8 (in log2 units), so
-// P <= 2^8 and the O rescale is skipped on almost every tile.  The final O / l
-// is unchanged by the choice of offset because l sums exactly the bf16 P values
-// that enter the P*V product.
+// LDS.  One 64 KiB array holds K and V tiles double-buffered, K one tile ahead
+// of V: during iteration t the waves read K(t+1) and V(t) while DMA
+// (buffer_load_dwordx4 ... lds, no VGPR staging) fills K(t+2) and V(t+1) into
+// the other two buffers; one barrier per tile.  The buffers sit at fixed offsets,
+// so the buffer choice folds into the ds_read immediate offset.  The DMA is
+// issued by inline asm and awaited explicitly (vmcnt(0)) before each tile
+// barrier: the compiler, which cannot prove that the in-flight writes miss the
+// buffers being read, would otherwise wait for them before every LDS read.
+// Tiles are stored row-major (one 256-byte row per key, sixteen 16-byte
+// chunks), chunk c of row r at physical chunk c ^ swz(r),
+// swz(r) = 4*(r & 3) + ((r >> 2) & 3).  The LDS has 64 four-byte banks and
+// serves 16 lanes of a 16-byte read, or 32 lanes of an 8-byte read, per cycle;
+// swz takes 16 distinct values over any 16 consecutive rows (the K operand
+// read) and distinct top bits over 4 consecutive rows (the transposed V read,
+// ds_read_b64_tr_b16: 32 lanes = 4 keys x 4 chunks), so both are conflict-free
+// (checked with the SQ_LDS_BANK_CONFLICT counter).
+//
+// Softmax rescaling is lazy: the exponent offset m only moves when a tile's
+// maximum exceeds it by more than 8 (log2 units), so P <= 2^8 and the O rescale
+// is skipped on almost every tile.  The row sum l adds exactly the bf16 P values
+// that enter the P*V product, so O / l is unaffected by the offset.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,18 +61,20 @@ namespace h3attn {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 
 constexpr int kD = 128;
-constexpr int kBM = 128;                 // query rows per workgroup
-constexpr int kBN = 64;                  // keys per tile
+constexpr int kBM = 128;                  // query rows per workgroup
+constexpr int kBN = 64;                   // keys per tile
 constexpr int kThreads = 256;
-constexpr int kTileBytes = kBN * kD * 2; // 16 KiB per K or V tile
+constexpr int kTileBytes = kBN * kD * 2;  // 16 KiB per K or V tile
+constexpr int kK0 = 0, kK1 = kTileBytes, kV0 = 2 * kTileBytes, kV1 = 3 * kTileBytes;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
@@ -69,9 +84,20 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2_t r;
-  r[0] = (__bf16)a;
+  r[0] = (__bf16)a;  // v_cvt_pk_bf16_f32: round to nearest even
   r[1] = (__bf16)b;
   return __builtin_bit_cast(uint32_t, r);
+}
+
+// Reduce over the lane pair (l, l ^ 32): with both operands = x, the swap
+// returns x of the lower half and x of the upper half in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
@@ -81,84 +107,151 @@ __device__ __forceinline__ int tile_offset(int row, int ch) {
   return row * (kD * 2) + ((((ch >> 3) ^ swz(row))) << 4) + ((ch & 7) << 1);
 }
 
-// DMA one 64-key tile of a [L][H][128] tensor into a swizzled LDS tile.  Each
-// wave writes four contiguous 1 KiB pieces (64 lanes x 16 B, lane-ordered);
-// lane `lane` of piece p fetches the global chunk that belongs at its slot.
-// The tile base is wave-uniform and each lane adds a fixed 32-bit byte offset
-// (row * token stride + chunk), so per tile only the scalar base moves.
+// ---------------------------------------------------------------- tile DMA
+// One 64-key tile of a [L][H][128] tensor goes into a swizzled LDS tile as 16
+// pieces of 1 KiB; wave w writes pieces w, w+4, w+8, w+12.  A piece is 64
+// lanes x 16 bytes in lane order at M0; lane `lane` fetches the global chunk
+// that belongs at its slot, at a fixed byte offset from the tile base.  The
+// load goes through a buffer resource whose size ends at the document's last
+// row: rows past it read as zeros (their scores are masked to -inf and their
+// V rows then contribute nothing), and no address outside the tensor is used.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kBufferDword3 = 0x00020000;  // raw buffer, 32-bit data format
+
 struct DmaOffsets {
   uint32_t off[4];
 };
 
-__device__ __forceinline__ DmaOffsets dma_offsets(int64_t tok_stride, int wave, int lane, int max_row) {
+__device__ __forceinline__ DmaOffsets dma_offsets(int64_t tok_stride, int wave, int lane) {
   DmaOffsets d;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int slot = (it * 4 + wave) * 64 + lane;  // 16-byte slot in the tile
     const int r = slot >> 4;
     const int c = (slot & 15) ^ swz(r);
-    // Rows past the end of the document re-read the last row (finite values;
-    // their scores are masked and their probabilities are zero).
-    d.off[it] = (uint32_t)(((int64_t)min(r, max_row) * tok_stride + 8 * c) * 2);
+    d.off[it] = (uint32_t)(((int64_t)r * tok_stride + 8 * c) * 2);
   }
   return d;
 }
 
-__device__ __forceinline__ void tile_dma(const char* tile_base, const DmaOffsets& d, lds_char* tile,
-                                         int wave) {
+// tile_base: first byte of the tile's row 0 (this head); valid_bytes: bytes
+// from there to the end of the document's last row of this head.
+__device__ __forceinline__ void tile_dma(const char* tile_base, int64_t valid_bytes, const DmaOffsets& d,
+                                         uint32_t lds_tile, int wave) {
+  const uint64_t b = (uint64_t)(uintptr_t)tile_base;
+  const uint32_t n = valid_bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)valid_bytes;
+  const i32x4_t rsrc = {(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
+                        (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)),
+                        (int)__builtin_amdgcn_readfirstlane(n), kBufferDword3};
 #pragma unroll
-  for (int it = 0; it < 4; ++it)
-    __builtin_amdgcn_global_load_lds(tile_base + d.off[it], tile + (it * 4 + wave) * 1024, 16, 0, 0);
+  for (int it = 0; it < 4; ++it) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_tile + (it * 4 + wave) * 1024);
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :
+                 : "v"(d.off[it]), "s"(m0), "s"(rsrc)
+                 : "memory");
+  }
 }
 
-// One tile: S^T, online softmax, O^T += V^T P^T.  kt/vt are the tile's LDS buffers.
-template <bool kTail>
-__device__ __forceinline__ void tile_step(const lds_char* kt, const lds_char* vt, const bf16x8_t (&qf)[8],
-                                          f32x16_t (&o)[4], float& m_run, float& l_run, int kbase,
-                                          int L, float c, int col, int g, int lane) {
-  // S^T[key][query] for the two 32-key blocks of the tile; the two accumulation
-  // chains are interleaved so consecutive MFMAs are independent.
-  f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+// All of this wave's tile DMA has landed in LDS.
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// Keeps the compiler from flattening a rarely taken branch into straight-line
+// selects executed on every tile.
+__device__ __forceinline__ void cold_path() { asm volatile("" ::: "memory"); }
+
+// ---------------------------------------------------------------- per-wave state
+struct State {
+  bf16x8_t q[8];   // Q^T operand: q[ks] = Q[row][16 ks + 8 g .. +7]
+  f32x16_t o[4];   // O^T accumulators, d-blocks of 32
+  bf16x8_t p[4];   // P^T operand of the current tile, four 16-key steps
+  float m;         // exponent offset (raw score units)
+  float l;         // this lane-half's partial sum of P
+};
+
+// LDS read addresses.  With the swizzle above, the k-step of a K read and the
+// d-block of a V read enter the byte offset through bits that no other term
+// touches, so each read address is a per-lane base XOR a constant (plus an
+// immediate for the 32-key block, the 16-key step and the buffer):
+//   K (row 32 kb + col, channels 16 ks + 8 g .. +7):
+//     kb * 8192 + (kaddr ^ 32 ks),  kaddr = 256 col + (16 g ^ 16 swz(col))
+//   V (row 16 j + 8 h + key_a, channels 32 dblk + ch .. +3):
+//     4096 j + (vaddr[h] ^ 64 dblk),
+//     vaddr[h] = 256 (8 h + key_a) + 8 ((ch >> 2) & 1) + (16 (ch >> 3) ^ 16 swz(8 h + key_a))
+// The bases are refreshed opaquely each iteration so the compiler derives the
+// addresses with one XOR each instead of keeping 28 of them live.
+struct Addr {
+  uint32_t k, v0, v1;
+};
+
+// S^T = K_tile Q^T (two interleaved accumulation chains).
+template <int kBuf>
+__device__ __forceinline__ void qk(f32x16_t (&s)[2], const State& st, const lds_char* lds, const Addr& a) {
+  s[0] = f32x16_t{};
+  s[1] = f32x16_t{};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
+    const uint32_t off = a.k ^ (32u * ks);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8_t a = *(const lds_bf16x8*)(kt + tile_offset(32 * kb + col, 16 * ks + 8 * g));
-      s[kb] = mfma32(a, qf[ks], s[kb]);
+      const bf16x8_t op = *(const lds_bf16x8*)(lds + kBuf + kb * 8192 + off);
+      s[kb] = mfma32(op, st.q[ks], s[kb]);
     }
   }
-  if (kTail) {  // keys past the end of the document do not exist
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          if (kbase + 32 * kb + 8 * r + 4 * g + qq >= L) s[kb][4 * r + qq] = -INFINITY;
-  }
+}
 
-  // Tile maximum of this lane's query over both lane-halves.
-  float mx = fmaxf(s[0][0], s[1][0]);
+// O^T += V_tile^T P^T.  The A operand for d-block dblk and 16-key step j comes
+// from two transposed reads: lane l (group G = l >> 4, index i = l & 15)
+// addresses key 16 j + 4 (G >> 1) + (i >> 2) (+8 for the second read) at
+// channel 32 dblk + 16 (G & 1) + 4 (i & 3), and receives keys {16 j + 4 g + e}
+// and {16 j + 8 + 4 g + e} of channel 32 dblk + (l % 32) -- the key order of
+// the P^T accumulator slots.
+template <int kBuf>
+__device__ __forceinline__ void pv(State& st, const lds_char* lds, const Addr& a) {
 #pragma unroll
-  for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s[0][e], s[1][e]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  // Move the exponent offset only when the tile would push P above 2^8.  Both
-  // lane-halves of a query see the same mx and m_run, so they decide alike.
-  const bool need = (mx - m_run) * c > kRescaleThreshold;
-  if (__any(need)) {
-    const float m_new = need ? mx : m_run;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);  // m_run = -inf on the first tile -> 0
-    l_run *= alpha;
+  for (int dblk = 0; dblk < 4; ++dblk) {
+    const uint32_t off0 = a.v0 ^ (64u * dblk), off1 = a.v1 ^ (64u * dblk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] *= alpha;
-    m_run = m_new;
+    for (int j = 0; j < 4; ++j) {
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + kBuf + 4096 * j + off0));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + kBuf + 4096 * j + off1));
+      const i16x8_t a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      st.o[dblk] = mfma32(__builtin_bit_cast(bf16x8_t, a16), st.p[j], st.o[dblk]);
+    }
   }
-  // P = 2^(s*c - m*c), rounded to bf16 for the P*V product.  The row sum adds
-  // the same rounded values (v_dot2_f32_bf16 against (1, 1)), so the output is
-  // an exact convex combination of V rows with the weights the MFMA used.
-  const float mc = m_run * c;
+}
+
+// Scores of keys at or past L (only in the last, partial tile) become -inf.
+__device__ __forceinline__ void mask_tail(f32x16_t (&s)[2], int kbase, int L, int g) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        if (kbase + 32 * kb + 8 * r + 4 * g + qq >= L) s[kb][4 * r + qq] = -INFINITY;
+}
+
+// Online softmax of s into st.p; returns whether any lane's offset moved, with
+// the rescale factor in alpha (the caller applies it to O before P*V).
+__device__ __forceinline__ bool softmax(const f32x16_t (&s)[2], State& st, float c, float& alpha) {
+  float m0 = fmaxf(s[0][0], s[0][1]);
+  float m1 = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+  for (int e = 2; e < 16; e += 2) {
+    m0 = fmaxf(fmaxf(m0, s[0][e]), s[0][e + 1]);  // v_max3_f32
+    m1 = fmaxf(fmaxf(m1, s[1][e]), s[1][e + 1]);
+  }
+  const float mx = pair_max(fmaxf(m0, m1));
+  // Both lane-halves of a query see the same mx and m, so they decide alike.
+  const bool need = (mx - st.m) * c > kRescaleThreshold;
+  const float m_new = need ? mx : st.m;
+  alpha = __builtin_amdgcn_exp2f((st.m - m_new) * c);  // 0 on the first tile, 1 if unchanged
+  st.m = m_new;
+  // P = 2^(s*c - m*c), rounded to bf16 for the P*V product; the row sum adds the
+  // same rounded values (v_dot2_f32_bf16 against (1, 1)).
+  const float mc = m_new * c;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  bf16x8_t pf[4];
   float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -167,43 +260,76 @@ __device__ __forceinline__ void tile_step(const lds_char* kt, const lds_char* vt
       bf16x2_t pr;
       pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][e], c, -mc));
       pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][e + 1], c, -mc));
-      psum[e >> 2 & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum[e >> 2 & 3], false);
-      pf[2 * kb + (e >> 3)][e & 7] = pr[0];
-      pf[2 * kb + (e >> 3)][(e & 7) + 1] = pr[1];
+      psum[(e >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum[(e >> 1) & 3], false);
+      st.p[2 * kb + (e >> 3)][e & 7] = pr[0];
+      st.p[2 * kb + (e >> 3)][(e & 7) + 1] = pr[1];
     }
-  l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+  st.l = fmaf(st.l, alpha, (psum[0] + psum[1]) + (psum[2] + psum[3]));
+  // Keep the exponentials here, next to the score MFMAs of the following tile,
+  // instead of letting them sink below the (rarely taken) rescale branch.
+  asm volatile("" : : "v"(st.p[0]), "v"(st.p[1]), "v"(st.p[2]), "v"(st.p[3]));
+  return __any(need);
+}
 
-  // O^T[d][query] += V^T[d][keys] * P^T[keys][query].  The A operand for d-block
-  // dblk and 16-key step st comes from two transposed reads: lane l (group
-  // G = l >> 4, index i = l & 15) addresses key 16*st + 4*(G >> 1) + (i >> 2)
-  // (+8 for the second read) at channel 32*dblk + 16*(G & 1) + 4*(i & 3), and
-  // receives keys {16 st + 4g + e} and {16 st + 8 + 4g + e} of channel
-  // 32*dblk + (l % 32) -- the same key order as the P^T accumulator slots.
-  const int G = lane >> 4, i = lane & 15;
-  const int key_a = 4 * (G >> 1) + (i >> 2);
-  const int ch = 16 * (G & 1) + 4 * (i & 3);
+__device__ __forceinline__ void rescale(State& st, float alpha) {
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
-#pragma unroll
-    for (int dblk = 0; dblk < 4; ++dblk) {
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vt + tile_offset(16 * st + key_a, 32 * dblk + ch)));
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vt + tile_offset(16 * st + 8 + key_a, 32 * dblk + ch)));
-      typedef short i16x8_t __attribute__((ext_vector_type(8)));
-      const i16x8_t a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[dblk] = mfma32(__builtin_bit_cast(bf16x8_t, a16), pf[st], o[dblk]);
-    }
+  for (int i = 0; i < 4; ++i) st.o[i] *= alpha;
+}
+
+// ---------------------------------------------------------------- kernel
+struct Ctx {
+  const lds_char* lds;
+  uint32_t lds_base;
+  const char* kbase;
+  const char* vbase;
+  int64_t tile_stride_bytes;  // 64 rows
+  int64_t row_bytes;          // one token row of all heads
+  DmaOffsets dma;
+  int n_full, n_tiles, L, wave, g;
+  float c;
+};
+
+__device__ __forceinline__ void dma(const Ctx& x, const char* base, int t, int buf) {
+  const int64_t valid = (int64_t)(x.L - 1 - t * kBN) * x.row_bytes + kD * 2;
+  tile_dma(base + t * x.tile_stride_bytes, valid, x.dma, x.lds_base + buf, x.wave);
+}
+
+// Iteration for tile t with a successor: S(t+1) from K(t+1) in kNext while the
+// softmax of S(t) runs, then O += V(t) P(t) from kVCur; DMA fills K(t+2) into
+// kKFill and V(t+1) into kVFill.  s_cur holds S(t) on entry; s_next receives
+// S(t+1).
+template <int kNext, int kVCur, int kKFill, int kVFill>
+__device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, f32x16_t (&s_cur)[2],
+                                          f32x16_t (&s_next)[2], int t) {
+  asm volatile("" : "+v"(a.k), "+v"(a.v0), "+v"(a.v1));
+  if (t + 2 < x.n_tiles) dma(x, x.kbase, t + 2, kKFill);
+  dma(x, x.vbase, t + 1, kVFill);
+  qk<kNext>(s_next, st, x.lds, a);
+  float alpha;
+  if (softmax(s_cur, st, x.c, alpha)) {
+    cold_path();
+    rescale(st, alpha);
   }
+  pv<kVCur>(st, x.lds, a);
+  if (t + 1 >= x.n_full) {
+    cold_path();
+    mask_tail(s_next, (t + 1) * kBN, x.L, x.g);
+  }
+  dma_wait();
+  __syncthreads();  // K(t+2), V(t+1) landed; every wave is done with K(t+1), V(t)
+}
+
+template <int kVCur>
+__device__ __forceinline__ void last_tile(const Ctx& x, State& st, const Addr& a, f32x16_t (&s_cur)[2]) {
+  float alpha;
+  if (softmax(s_cur, st, x.c, alpha)) rescale(st, alpha);
+  pv<kVCur>(st, x.lds, a);
 }
 
 __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, int L, int H, float scale_log2e, int n_qtiles) {
-  __shared__ __attribute__((aligned(1024))) char k_lds0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_lds0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_raw[4 * kTileBytes];
 
   // Workgroups are dispatched round-robin over the 8 XCDs (block b -> XCD b%8).
   // Renumber so each XCD receives a contiguous run of (head, q-tile) work:
@@ -217,84 +343,85 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31, g = lane >> 5;
-  const int64_t tok_stride = (int64_t)H * kD;  // elements between consecutive tokens
-  const uint16_t* kh = k + (int64_t)head * kD;
-  const uint16_t* vh = v + (int64_t)head * kD;
+  Ctx x;
+  x.lds = (const lds_char*)lds_raw;
+  x.lds_base = (uint32_t)(uintptr_t)(lds_char*)lds_raw;
+  x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  x.g = lane >> 5;
+  x.L = L;
+  x.c = scale_log2e;
+  const int64_t tok_stride = (int64_t)H * kD;      // elements between consecutive tokens
+  x.row_bytes = tok_stride * 2;
+  x.n_full = L / kBN;                              // tiles with 64 real keys
+  x.n_tiles = (L + kBN - 1) / kBN;                 // plus one partial tile if L % 64 != 0
+  x.tile_stride_bytes = (int64_t)kBN * x.row_bytes;
+  x.kbase = reinterpret_cast<const char*>(k + (int64_t)head * kD);
+  x.vbase = reinterpret_cast<const char*>(v + (int64_t)head * kD);
+  x.dma = dma_offsets(tok_stride, x.wave, lane);
 
-  const int n_full = L / kBN;                 // tiles with 64 real keys
-  const int n_tiles = (L + kBN - 1) / kBN;    // plus one partial tile if L % 64 != 0
-  const int64_t tile_stride_bytes = (int64_t)kBN * tok_stride * 2;
-  const char* kbase_ptr = reinterpret_cast<const char*>(kh);
-  const char* vbase_ptr = reinterpret_cast<const char*>(vh);
-  const DmaOffsets dma_full = dma_offsets(tok_stride, wave, lane, kBN - 1);
-  const DmaOffsets dma_tail = dma_offsets(tok_stride, wave, lane, (L - 1) % kBN);
-  auto dma = [&](int t, lds_char* kt, lds_char* vt) {
-    const DmaOffsets& d = (t < n_full) ? dma_full : dma_tail;
-    tile_dma(kbase_ptr + t * tile_stride_bytes, d, kt, wave);
-    tile_dma(vbase_ptr + t * tile_stride_bytes, d, vt, wave);
-  };
-  dma(0, (lds_char*)k_lds0, (lds_char*)v_lds0);
+  Addr a;
+  a.k = 256u * col + ((16u * x.g) ^ (16u * swz(col)));
+  {
+    const int key_a = 4 * (lane >> 5) + ((lane & 15) >> 2);  // transposed-read key of this lane
+    const int ch = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // transposed-read channel
+    a.v0 = 256u * key_a + 8u * ((ch >> 2) & 1) + ((16u * (ch >> 3)) ^ (16u * swz(key_a)));
+    a.v1 = 256u * (8 + key_a) + 8u * ((ch >> 2) & 1) + ((16u * (ch >> 3)) ^ (16u * swz(8 + key_a)));
+  }
+
+  dma(x, x.kbase, 0, kK0);
+  dma(x, x.vbase, 0, kV0);
+  if (x.n_tiles > 1) dma(x, x.kbase, 1, kK1);
 
   // Q^T operand: lane holds Q[row][16ks + 8g .. +7] for its query row.
-  const int qrow = qtile * kBM + wave * 32 + col;
-  bf16x8_t qf[8];
+  State st;
+  const int qrow = qtile * kBM + x.wave * 32 + col;
   if (qrow < L) {
-    const uint16_t* p = q + (int64_t)qrow * tok_stride + (int64_t)head * kD + 8 * g;
+    const uint16_t* p = q + (int64_t)qrow * tok_stride + (int64_t)head * kD + 8 * x.g;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(p + 16 * ks);
+    for (int ks = 0; ks < 8; ++ks) st.q[ks] = *reinterpret_cast<const bf16x8_t*>(p + 16 * ks);
   } else {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = bf16x8_t{};
+    for (int ks = 0; ks < 8; ++ks) st.q[ks] = bf16x8_t{};
   }
-
-  f32x16_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x16_t{};
-  float m_run = -INFINITY;  // exponent offset (raw score units) for this lane's query
-  float l_run = 0.f;        // this lane-half's partial sum of P
-  auto full_step = [&](int t, const lds_char* kt, const lds_char* vt) {
-    tile_step<false>(kt, vt, qf, o, m_run, l_run, t * kBN, L, scale_log2e, col, g, lane);
-  };
-  __syncthreads();          // tile 0 is in LDS
+  for (int i = 0; i < 4; ++i) st.o[i] = f32x16_t{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  dma_wait();
+  __syncthreads();  // K(0), V(0), K(1) are in LDS
 
-  // Full tiles, two per trip so each buffer is named statically; the loop body
-  // is one straight path.  The partial tile (if L % 64 != 0) is peeled below.
+  f32x16_t s0[2], s1[2];
+  qk<kK0>(s0, st, x.lds, a);
+  if (x.n_full == 0) mask_tail(s0, 0, L, x.g);
+
+  // Iteration t (t = 0 .. n_tiles-2) reads K(t+1) from buffer (t+1)%2 and V(t)
+  // from buffer t%2; two iterations per trip keep both parities and both score
+  // buffers static, and an odd count leaves one even iteration.
   int t = 0;
-  for (; t + 1 < n_full; t += 2) {
-    dma(t + 1, (lds_char*)k_lds1, (lds_char*)v_lds1);
-    full_step(t, (const lds_char*)k_lds0, (const lds_char*)v_lds0);
-    __syncthreads();  // tile t+1 landed; every wave is done with buffer 0
-    if (t + 2 < n_tiles) dma(t + 2, (lds_char*)k_lds0, (lds_char*)v_lds0);
-    full_step(t + 1, (const lds_char*)k_lds1, (const lds_char*)v_lds1);
-    __syncthreads();  // tile t+2 landed; every wave is done with buffer 1
+  for (; t + 2 < x.n_tiles; t += 2) {
+    iteration<kK1, kV0, kK0, kV1>(x, st, a, s0, s1, t);
+    iteration<kK0, kV1, kK1, kV0>(x, st, a, s1, s0, t + 1);
   }
-  if (t < n_full) {  // odd number of full tiles: the last one sits in buffer 0
-    if (t + 1 < n_tiles) dma(t + 1, (lds_char*)k_lds1, (lds_char*)v_lds1);
-    full_step(t, (const lds_char*)k_lds0, (const lds_char*)v_lds0);
-    __syncthreads();
-    ++t;
-  }
-  if (t < n_tiles) {  // the partial tile, in buffer t % 2
-    const lds_char* kt = (t & 1) ? (const lds_char*)k_lds1 : (const lds_char*)k_lds0;
-    const lds_char* vt = (t & 1) ? (const lds_char*)v_lds1 : (const lds_char*)v_lds0;
-    tile_step<true>(kt, vt, qf, o, m_run, l_run, t * kBN, L, scale_log2e, col, g, lane);
+  if (t + 1 < x.n_tiles) {
+    iteration<kK1, kV0, kK0, kV1>(x, st, a, s0, s1, t);
+    last_tile<kV1>(x, st, a, s1);
+  } else {
+    last_tile<kV0>(x, st, a, s0);
   }
 
   // Epilogue: full row sum = both lane-halves; O / l -> bf16.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv_l = 1.0f / l_tot;
+  const float inv_l = 1.0f / pair_sum(st.l);
   if (qrow < L) {
     uint16_t* po = out + (int64_t)qrow * tok_stride + (int64_t)head * kD;
 #pragma unroll
     for (int dblk = 0; dblk < 4; ++dblk)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int d = 32 * dblk + 8 * r + 4 * g;
+        const int d = 32 * dblk + 8 * r + 4 * x.g;
         *reinterpret_cast<uint2*>(po + d) =
-            make_uint2(pack_bf16x2(o[dblk][4 * r] * inv_l, o[dblk][4 * r + 1] * inv_l),
-                       pack_bf16x2(o[dblk][4 * r + 2] * inv_l, o[dblk][4 * r + 3] * inv_l));
+            make_uint2(pack_bf16x2(st.o[dblk][4 * r] * inv_l, st.o[dblk][4 * r + 1] * inv_l),
+                       pack_bf16x2(st.o[dblk][4 * r + 2] * inv_l, st.o[dblk][4 * r + 3] * inv_l));
       }
   }
 }
