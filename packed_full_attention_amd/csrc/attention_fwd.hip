@@ -394,6 +394,10 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
   f32x16_t s0[2], s1[2];
   qk<kK0>(s0, st, x.lds, a);
   if (x.n_full == 0) mask_tail(s0, 0, L, x.g);
+  // The first iteration refills buffer K0 with K(2): every wave must be done
+  // reading K(0) first.  (Later refills are ordered by the previous
+  // iteration's barrier.)
+  __syncthreads();
 
   // Iteration t (t = 0 .. n_tiles-2) reads K(t+1) from buffer (t+1)%2 and V(t)
   // from buffer t%2; two iterations per trip keep both parities and both score
