@@ -10,10 +10,19 @@
 // atomics; every output row is produced by exactly one wave, so the result
 // does not depend on the grid or on the number of CUs.
 //
-// Work decomposition.  A 256-thread workgroup owns BM = 128 query rows of one
-// head; each of its 4 waves owns 32 of them, and two workgroups share a CU (two
-// waves per SIMD).  Keys stream through LDS in tiles of BN = 64.  Per tile a
-// wave computes
+// Two launches.  v_transpose_kernel writes V^T, [H][128][Lp] with Lp = L
+// rounded up to 64 and zeros past L, into the caller's workspace; the
+// attention kernel then reads K from [L][H][128] and V^T from the workspace.
+// The transposed copy lets every P*V operand be one 16-byte LDS read: the
+// transposing LDS read (ds_read_b64_tr_b16) that would otherwise build the
+// operand from row-major V moves a quarter of the bytes per cycle that
+// ds_read_b128 does on gfx950, and with it the LDS, not the matrix cores,
+// bounded the kernel.  The copy costs one extra HBM pass over V.
+//
+// Work decomposition.  A 512-thread workgroup owns BM = 256 query rows of one
+// head; each of its 8 waves owns 32 of them (two waves per SIMD, one workgroup
+// per CU).  Keys stream through LDS in tiles of BN = 64, shared by all 8
+// waves.  Per tile a wave computes
 //   S^T = K_tile * Q^T        (v_mfma_f32_32x32x16_bf16, 2 x 8)
 //   softmax weights of S^T    (fp32; exp2 with scale*log2(e) folded into an FMA)
 //   O^T += V_tile^T * P^T     (v_mfma_f32_32x32x16_bf16, 4 x 4)
@@ -23,36 +32,44 @@
 // trip for P), and the row statistics need one cross-half exchange
 // (v_permlane32_swap, no LDS).
 //
+// Key order.  The B operand of a 32x32x16 MFMA takes k-slots 8g .. 8g+7 from
+// lane half g; the P^T operand built from S^T accumulator rows holds, in those
+// slots, tile rows 16j + {4g .. 4g+3, 8+4g .. 11+4g}.  The V^T operand read as
+// one 16-byte chunk holds keys 16j + 8g .. 16j + 8g + 7.  The two agree because
+// the K tile is stored with its rows permuted: LDS row r of a K tile holds key
+// perm(r), perm swapping bits 2 and 3 of r (an involution within each group of
+// 16 keys).
+//
 // Software pipeline.  Iteration t issues
 //   S(t+1) = K(t+1) Q^T        (matrix cores)
 //   O += V(t-1)^T P(t-1)^T     (matrix cores)
 //   P(t) = exp2(c S(t) - c m)  (VALU + transcendental unit)
 // None of the three depends on another, so the 32 matrix instructions of an
-// iteration are spread evenly through its ~100 vector instructions (the
-// sched_group_barrier pattern below): a matrix instruction runs for 32 cycles,
-// during which the same SIMD executes about three independent VALU
-// instructions of this or of the other wave at no cost.
+// iteration are spread evenly through its ~100 vector instructions: a matrix
+// instruction runs for 32 cycles, during which the same SIMD executes about
+// three independent VALU instructions of this or of the other wave at no cost.
 //
-// LDS.  One 64 KiB array holds K and V tiles double-buffered: during iteration
-// t the waves read K(t+1) and V(t-1) while DMA (buffer_load_dwordx4 ... lds,
-// no VGPR staging) fills K(t+2) and V(t) into the other two buffers; one
-// barrier per tile.  The buffers sit at fixed offsets, so the buffer choice
-// folds into the ds_read immediate offset.  The DMA is issued by inline asm and
-// awaited explicitly (vmcnt(0)) before each tile barrier: the compiler, which
-// cannot prove that the in-flight writes miss the buffers being read, would
-// otherwise wait for them before every LDS read.  Tiles are stored row-major
-// (one 256-byte row per key, sixteen 16-byte chunks), chunk c of row r at
-// physical chunk c ^ swz(r), swz(r) = 4*(r & 3) + ((r >> 2) & 3).  The LDS has
-// 64 four-byte banks and serves 16 lanes of a 16-byte read, or 32 lanes of an
-// 8-byte read, per cycle; swz takes 16 distinct values over any 16 consecutive
-// rows (the K operand read) and distinct top bits over 4 consecutive rows (the
-// transposed V read, ds_read_b64_tr_b16: 32 lanes = 4 keys x 4 chunks), so
-// both are conflict-free (checked with the SQ_LDS_BANK_CONFLICT counter).
+// LDS.  Two rings of three 16 KiB tiles, K and V^T: during iteration t the
+// waves read K(t+1) and V^T(t-1) while DMA (buffer_load_dwordx4 ... lds, no
+// VGPR staging) fills K(t+3) and V^T(t+1), each into the slot its ring freed
+// in iteration t-1; one barrier per tile, and a DMA has two iterations to land.
+// The DMA is issued by inline asm and awaited explicitly (vmcnt) before each
+// tile barrier: the compiler, which cannot prove that the in-flight writes miss
+// the buffers being read, would otherwise wait for them before every LDS read.
+// Layouts (64 four-byte banks; a 16-byte read serves 16 lanes per cycle, so
+// each group of 16 lanes must cover all 64 banks):
+//   K tile: 64 rows x 256 bytes (sixteen 16-byte chunks), chunk c of row r at
+//     physical chunk c ^ swz(r), swz(r) = 4 (r & 3) + ((r >> 2) & 3), which
+//     takes 16 distinct values over any 16 consecutive rows (the K operand
+//     read: 16 lanes = 16 rows, one chunk);
+//   V^T tile: 128 rows (channels) x 128 bytes (eight chunks of 8 keys), chunk
+//     c of row d at physical chunk c ^ ((d >> 1) & 7): 16 consecutive rows then
+//     fill 16 distinct 16-byte bank groups.
 //
 // Exponent offset.  The weights of a tile are computed against the offset m
 // the row already has, with no per-tile maximum.  Each lane adds up the bf16
-// weights it produced (v_dot2_f32_bf16 against (1, 1): exactly the values that
-// enter the P*V product, so O / l does not depend on m).  If some lane's sum
+// weights it produced (exactly the values that enter the P*V product, so O / l
+// does not depend on m).  If some lane's sum
 // exceeds 2^8 (so some weight may exceed 2^8, or overflowed), the wave takes a
 // rare path: m moves to the row maximum of the tile, the already accumulated O
 // and l are scaled by 2^(c (m_old - m_new)), and the tile's weights are
@@ -70,18 +87,19 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 
 constexpr int kD = 128;
-constexpr int kBM = 128;                  // query rows per workgroup
+constexpr int kWaves = 8;                 // waves per workgroup, 32 query rows each
+constexpr int kBM = 32 * kWaves;          // query rows per workgroup
 constexpr int kBN = 64;                   // keys per tile
-constexpr int kThreads = 256;
-constexpr int kTileBytes = kBN * kD * 2;  // 16 KiB per K or V tile
-constexpr int kK0 = 0, kK1 = kTileBytes, kV0 = 2 * kTileBytes, kV1 = 3 * kTileBytes;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kDmaPerWave = 16 / kWaves;  // 1 KiB DMA pieces per wave per tile
+constexpr int kTileBytes = kBN * kD * 2;  // 16 KiB per K or V^T tile
+constexpr int kStages = 3;                // tiles per ring (resident or in flight)
+constexpr int kVRing = kStages * kTileBytes;  // the V^T ring follows the K ring
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSumBound = 256.0f;        // a lane's tile sum of P above this moves the offset
 
@@ -108,41 +126,51 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-
-// Byte offset of (row, channel) in a swizzled tile; channel % 4 == 0.
-__device__ __forceinline__ int tile_offset(int row, int ch) {
-  return row * (kD * 2) + ((((ch >> 3) ^ swz(row))) << 4) + ((ch & 7) << 1);
-}
+__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
+// Key held by row r of a K tile (and by S^T accumulator row r).
+__device__ __forceinline__ int perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 // ---------------------------------------------------------------- tile DMA
-// One 64-key tile of a [L][H][128] tensor goes into a swizzled LDS tile as 16
-// pieces of 1 KiB; wave w writes pieces w, w+4, w+8, w+12.  A piece is 64
-// lanes x 16 bytes in lane order at M0; lane `lane` fetches the global chunk
-// that belongs at its slot, at a fixed byte offset from the tile base.  The
-// load goes through a buffer resource whose size ends at the document's last
-// row: rows past it read as zeros (their scores are masked to -inf and their
-// V rows then contribute nothing), and no address outside the tensor is used.
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// A 16 KiB tile goes into LDS as 16 pieces of 1 KiB; wave w writes pieces w and
+// w+8.  A piece is 64 lanes x 16 bytes in lane order at M0; each lane fetches
+// the global chunk that belongs at its slot, at a fixed byte offset from the
+// tile base.  Loads go through a buffer resource whose size ends at the last
+// valid byte: K rows past the document read as zeros (their scores are masked
+// to -inf), and no address outside the tensors is used.
 constexpr int kBufferDword3 = 0x00020000;  // raw buffer, 32-bit data format
 
 struct DmaOffsets {
-  uint32_t off[4];
+  uint32_t off[kDmaPerWave];
 };
 
-__device__ __forceinline__ DmaOffsets dma_offsets(int64_t tok_stride, int wave, int lane) {
+// K tile: slot (row r, physical chunk p) <- key perm(r), channels 8 (p ^ swz(r)) .. +7.
+__device__ __forceinline__ DmaOffsets k_dma_offsets(int64_t tok_stride, int wave, int lane) {
   DmaOffsets d;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int slot = (it * 4 + wave) * 64 + lane;  // 16-byte slot in the tile
+  for (int it = 0; it < kDmaPerWave; ++it) {
+    const int slot = (it * kWaves + wave) * 64 + lane;  // 16-byte slot in the tile
     const int r = slot >> 4;
     const int c = (slot & 15) ^ swz(r);
-    d.off[it] = (uint32_t)(((int64_t)r * tok_stride + 8 * c) * 2);
+    d.off[it] = (uint32_t)(((int64_t)perm(r) * tok_stride + 8 * c) * 2);
   }
   return d;
 }
 
-// tile_base: first byte of the tile's row 0 (this head); valid_bytes: bytes
-// from there to the end of the document's last row of this head.
+// V^T tile: slot (row d, physical chunk p) <- channel d, keys 8 (p ^ vswz(d)) .. +7.
+__device__ __forceinline__ DmaOffsets vt_dma_offsets(int64_t vt_row_bytes, int wave, int lane) {
+  DmaOffsets d;
+#pragma unroll
+  for (int it = 0; it < kDmaPerWave; ++it) {
+    const int slot = (it * kWaves + wave) * 64 + lane;
+    const int r = slot >> 3;
+    const int c = (slot & 7) ^ vswz(r);
+    d.off[it] = (uint32_t)(r * vt_row_bytes + 16 * c);
+  }
+  return d;
+}
+
+// tile_base: first byte of the tile; valid_bytes: bytes from there to the end
+// of the valid data.
 __device__ __forceinline__ void tile_dma(const char* tile_base, int64_t valid_bytes, const DmaOffsets& d,
                                          uint32_t lds_tile, int wave) {
   const uint64_t b = (uint64_t)(uintptr_t)tile_base;
@@ -151,22 +179,29 @@ __device__ __forceinline__ void tile_dma(const char* tile_base, int64_t valid_by
                         (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)),
                         (int)__builtin_amdgcn_readfirstlane(n), kBufferDword3};
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_tile + (it * 4 + wave) * 1024);
-    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+  for (int it = 0; it < kDmaPerWave; ++it) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_tile + (it * kWaves + wave) * 1024);
+    // One wait state between writing M0 and the LDS-DMA instruction that reads it.
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
                  :
                  : "v"(d.off[it]), "s"(m0), "s"(rsrc)
                  : "memory");
   }
 }
 
+// s_waitcnt immediate for vmcnt(n) (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 // All of this wave's tile DMA has landed in LDS.
-__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); }
+
+// All but this wave's n most recent DMA instructions have landed in LDS.
+template <int n>
+__device__ __forceinline__ void dma_wait_all_but() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(n)); }
 
 // Keeps the compiler from flattening a rarely taken branch into straight-line
 // selects executed on every tile.
 __device__ __forceinline__ void cold_path() { asm volatile("" ::: "memory"); }
-
 
 // ---------------------------------------------------------------- per-wave state
 struct State {
@@ -176,68 +211,74 @@ struct State {
   float l;         // this lane-half's partial sum of P
 };
 
-// LDS read addresses.  With the swizzle above, the k-step of a K read and the
-// d-block of a V read enter the byte offset through bits that no other term
-// touches, so each read address is a per-lane base XOR a constant (plus an
-// immediate for the 32-key block, the 16-key step and the buffer):
+// LDS read addresses.  The k-step of a K read and the key step of a V^T read
+// enter the byte offset through bits that no other term touches, so each read
+// address is a per-lane base XOR a constant, plus an immediate:
 //   K (row 32 kb + col, channels 16 ks + 8 g .. +7):
-//     kb * 8192 + (kaddr ^ 32 ks),  kaddr = 256 col + (16 g ^ 16 swz(col))
-//   V (row 16 j + 8 h + key_a, channels 32 dblk + ch .. +3):
-//     4096 j + (vaddr[h] ^ 64 dblk),
-//     vaddr[h] = 256 (8 h + key_a) + 8 ((ch >> 2) & 1) + (16 (ch >> 3) ^ 16 swz(8 h + key_a))
-// The bases are refreshed opaquely each iteration so the compiler derives the
-// addresses with one XOR each instead of keeping 28 of them live.
+//     kb * 8192 + (kaddr ^ 32 ks),  kaddr = buf + 256 col + (16 g ^ 16 swz(col))
+//   V^T (row 32 dblk + col, keys 16 j + 8 g .. +7):
+//     dblk * 4096 + (vaddr ^ 32 j),  vaddr = buf + 128 col + 16 (g ^ vswz(col))
+// The buffer offset buf is a multiple of 16 KiB and does not meet the XOR.
 struct Addr {
-  uint32_t k, v0, v1;
+  uint32_t k, v;
 };
 
-// One MFMA of S^T = K_tile Q^T: 32-key block kb, k-step ks.
-template <int kBuf>
-__device__ __forceinline__ void qk_step(f32x16_t& s, int kb, int ks, const State& st, const lds_char* lds,
-                                        const Addr& a) {
-  const bf16x8_t op = *(const lds_bf16x8*)(lds + kBuf + kb * 8192 + (a.k ^ (32u * ks)));
-  s = mfma32(op, st.q[ks], s);
+__device__ __forceinline__ Addr at_buffers(const Addr& a, uint32_t kbuf, uint32_t vbuf) {
+  return Addr{a.k + kbuf, a.v + vbuf};
 }
 
-// One MFMA of O^T += V_tile^T P^T: d-block dblk, 16-key step j.  The A operand
-// comes from two transposed reads: lane l (group G = l >> 4, index i = l & 15)
-// addresses key 16 j + 4 (G >> 1) + (i >> 2) (+8 for the second read) at
-// channel 32 dblk + 16 (G & 1) + 4 (i & 3), and receives keys {16 j + 4 g + e}
-// and {16 j + 8 + 4 g + e} of channel 32 dblk + (l % 32) -- the key order of
-// the P^T accumulator slots.
-template <int kBuf>
-__device__ __forceinline__ void pv_step(State& st, int dblk, int j, const bf16x8_t (&p)[4], const lds_char* lds,
-                                        const Addr& a) {
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(lds + kBuf + 4096 * j + (a.v0 ^ (64u * dblk))));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(lds + kBuf + 4096 * j + (a.v1 ^ (64u * dblk))));
-  const i16x8_t a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  st.o[dblk] = mfma32(__builtin_bit_cast(bf16x8_t, a16), p[j], st.o[dblk]);
+// Operand of the score MFMA for 32-key block kb, k-step ks.
+__device__ __forceinline__ bf16x8_t k_operand(int kb, int ks, const lds_char* lds, const Addr& b) {
+  return *(const lds_bf16x8*)(lds + kb * 8192 + (b.k ^ (32u * ks)));
 }
 
-template <int kBuf>
-__device__ __forceinline__ void pv(State& st, const bf16x8_t (&p)[4], const lds_char* lds, const Addr& a) {
+// Operand of the P*V MFMA for d-block dblk, 16-key step j.
+__device__ __forceinline__ bf16x8_t v_operand(int dblk, int j, const lds_char* lds, const Addr& b) {
+  return *(const lds_bf16x8*)(lds + dblk * 4096 + (b.v ^ (32u * j)));
+}
+
+// O^T += V_tile^T P^T.
+__device__ __forceinline__ void pv(State& st, const bf16x8_t (&p)[4], const lds_char* lds, const Addr& b) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int dblk = 0; dblk < 4; ++dblk) pv_step<kBuf>(st, dblk, j, p, lds, a);
+    for (int dblk = 0; dblk < 4; ++dblk) st.o[dblk] = mfma32(v_operand(dblk, j, lds, b), p[j], st.o[dblk]);
 }
 
-// Weights of score pair i (i = 0..15: block kb = i / 8, slots 2 (i % 8), +1)
-// against offset mc = c m: P = 2^(c s - mc), rounded to bf16 for the P*V
-// product; the lane sum adds the same rounded values (v_dot2_f32_bf16 against
-// (1, 1)) into one of four partial sums.
-__device__ __forceinline__ void weight_pair(const f32x16_t (&s)[2], int i, float c, float mc, bf16x8_t (&p)[4],
-                                            float (&ps)[4]) {
-  const int kb = i >> 3, e = 2 * (i & 7);
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  bf16x2_t pr;
-  pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][e], c, -mc));
-  pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][e + 1], c, -mc));
-  ps[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps[i & 3], false);
-  p[2 * kb + (e >> 3)][e & 7] = pr[0];
-  p[2 * kb + (e >> 3)][(e & 7) + 1] = pr[1];
+// Weights.  Score n (0..31) of a lane is accumulator slot n % 16 of block
+// n / 16; its weight P = 2^(c s - mc) (mc = c m) is rounded to bf16 and paired
+// with its neighbour: pair i = n / 2 is dword i % 4 of the P^T operand p[i / 4]
+// (low half: the even score).  The lane sum adds exactly these bf16 values,
+// read back from the packed pair -- the high half as a float is
+// (bits & 0xffff0000), the low half (bits << 16) -- with plain fp32 adds, which
+// the SIMD issues alongside the matrix instructions (a v_dot2_f32_bf16 against
+// (1, 1) would add the same values but stalls the matrix pipe).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+
+__device__ __forceinline__ void store_pairs(const uint32_t (&w)[16], bf16x8_t (&p)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    p[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]});
+}
+
+// All 32 weights of a tile and their lane sum (the unscheduled form, for the
+// first tile and the rare path).
+__device__ __forceinline__ float weights(const f32x16_t (&s)[2], float c, float mc, bf16x8_t (&p)[4]) {
+  uint32_t w[16];
+  float hi = 0.f, lo = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int kb = i >> 3, e = 2 * (i & 7);
+    w[i] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[kb][e], c, -mc)),
+                       __builtin_amdgcn_exp2f(fmaf(s[kb][e + 1], c, -mc)));
+    hi += hi_bf16(w[i]);
+    lo += lo_bf16(w[i]);
+  }
+  store_pairs(w, p);
+  return hi + lo;
 }
 
 // Rare path: move the offset to the row maximum of this tile (or keep it if
@@ -262,14 +303,12 @@ __device__ __forceinline__ float rebase(const f32x16_t (&s_in)[2], State& st, fl
   st.l *= alpha;
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.o[i] *= alpha;
-  float ps[4] = {0.f, 0.f, 0.f, 0.f};
-  const float mc = m_new * c;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) weight_pair(s, i, c, mc, p, ps);
-  return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  return weights(s, c, m_new * c, p);
 }
 
 // Scores of keys at or past L (only in the last, partial tile) become -inf.
+// Accumulator slot 4r + qq of lane half g is tile row 32 kb + 8 r + 4 g + qq,
+// which holds key perm(row).
 __device__ __forceinline__ void mask_tail(f32x16_t (&s)[2], int kbase, int L, int g) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -277,119 +316,120 @@ __device__ __forceinline__ void mask_tail(f32x16_t (&s)[2], int kbase, int L, in
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
-        if (kbase + 32 * kb + 8 * r + 4 * g + qq >= L) s[kb][4 * r + qq] = -INFINITY;
+        if (kbase + perm(32 * kb + 8 * r + 4 * g + qq) >= L) s[kb][4 * r + qq] = -INFINITY;
 }
 
 // ---------------------------------------------------------------- kernel
 struct Ctx {
   const lds_char* lds;
   uint32_t lds_base;
-  const char* kbase;
-  const char* vbase;
-  int64_t tile_stride_bytes;  // 64 rows
+  const char* kbase;          // K, this head, token 0
+  const char* vtbase;         // V^T, this head, channel 0, key 0
+  int64_t k_tile_bytes;       // 64 tokens of K
   int64_t row_bytes;          // one token row of all heads
-  DmaOffsets dma;
+  int64_t vt_valid;           // bytes from a V^T tile's first byte to its last
+  DmaOffsets kdma, vdma;
   int n_full, n_tiles, L, wave, g;
   float c;
 };
 
-__device__ __forceinline__ void dma(const Ctx& x, const char* base, int t, int buf) {
+// DMA of tile t (clamped to the last tile: the refetch past the end keeps the
+// number of DMA instructions per iteration fixed) into the LDS buffer at
+// byte offset buf of the K or V^T ring.
+__device__ __forceinline__ void dma_k(const Ctx& x, int t, uint32_t buf) {
+  t = t < x.n_tiles ? t : x.n_tiles - 1;
   const int64_t valid = (int64_t)(x.L - 1 - t * kBN) * x.row_bytes + kD * 2;
-  tile_dma(base + t * x.tile_stride_bytes, valid, x.dma, x.lds_base + buf, x.wave);
+  tile_dma(x.kbase + t * x.k_tile_bytes, valid, x.kdma, x.lds_base + buf, x.wave);
 }
+__device__ __forceinline__ void dma_vt(const Ctx& x, int t, uint32_t buf) {
+  t = t < x.n_tiles ? t : x.n_tiles - 1;
+  tile_dma(x.vtbase + t * (kBN * 2), x.vt_valid, x.vdma, x.lds_base + kVRing + buf, x.wave);
+}
+
+__device__ __forceinline__ uint32_t ring(int t) { return (uint32_t)(t % kStages) * kTileBytes; }
 
 // The 32 matrix instructions of an iteration, in issue order ("slots"): even
 // slot k is score MFMA k/2 (block kb = (k/2) & 1, k-step ks = k/4), odd slot k
 // is P*V MFMA (k-1)/2 (16-key step j = k/8, d-block (k/2) & 3).  Chains of
 // dependent MFMAs are 4 (scores) or 8 (P*V) slots apart.
-template <int kKNext, int kVPrev>
-__device__ __forceinline__ bf16x8_t slot_operand(int k, const lds_char* lds, const Addr& a) {
+__device__ __forceinline__ bf16x8_t slot_operand(int k, const lds_char* lds, const Addr& b) {
   const int i = k >> 1;
-  if ((k & 1) == 0) return *(const lds_bf16x8*)(lds + kKNext + (i & 1) * 8192 + (a.k ^ (32u * (i >> 1))));
-  const int j = i >> 2, dblk = i & 3;
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(lds + kVPrev + 4096 * j + (a.v0 ^ (64u * dblk))));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(lds + kVPrev + 4096 * j + (a.v1 ^ (64u * dblk))));
-  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return (k & 1) == 0 ? k_operand(i & 1, i >> 1, lds, b) : v_operand(i & 3, i >> 2, lds, b);
 }
 
-// Iteration t: S(t+1) from K(t+1) in buffer kKNext into s_next; O += V(t-1)
-// P(t-1) from buffer kVPrev (skipped for t = 0); P(t) from s_cur into p_cur.
-// DMA fills K(t+2) into kKFill (when it exists) and V(t) into kVFill.  In the
-// last iteration there is no K(t+1): S(t+1) is computed from the stale buffer
-// and never used.
+// Iteration t: S(t+1) from K(t+1) into s_next; O += V(t-1) P(t-1) (skipped for
+// t = 0); P(t) from s_cur into p_cur.  K(t+1) sits in ring slot (t+1) % 3 and
+// V^T(t-1) in slot (t-1) % 3.  DMA fills K(t+3) into the K slot of K(t) (read
+// in iteration t-1) and V^T(t+1) into the V slot of V^T(t-2) (read in
+// iteration t-1); the previous iteration's DMA (K(t+2), V^T(t)) must have
+// landed before the barrier that ends this one.  In the last iteration there
+// is no K(t+1): S(t+1) is computed from a stale slot and never used.
 //
 // With the P*V product (t > 0) the instruction order is fixed by hand, slot by
-// slot, with scheduling barriers in between: the operand reads of slot k + 2,
-// the MFMA of slot k, then a share of the weights -- the two FMAs of score
-// pair k/2 on even slots (plus the bf16 pack and row-sum of pair k/2 - 1), the
-// two exponentials of pair k/2 on odd slots.  Each slot then holds about one
-// MFMA's worth (32 cycles) of vector work, and every dependency is at least one
-// MFMA apart.
-template <int kKNext, int kVPrev, int kKFill, int kVFill, bool kPV>
+// slot, with scheduling barriers in between: the operand read of slot k + 2,
+// the MFMA of slot k, then a share of the weights, each step one slot after
+// the one it depends on -- the FMA of score k, the exponential of score k - 1,
+// on odd slots the bf16 pack of pair (k - 3) / 2, and the row-sum terms of the
+// pairs before it.  A slot then holds one transcendental and three or four
+// plain VALU instructions, which the SIMD executes under the 32-cycle matrix
+// instruction; four more slots without a matrix instruction finish the last
+// pairs.
+template <bool kPV>
 __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, const f32x16_t (&s_cur)[2],
                                           f32x16_t (&s_next)[2], const bf16x8_t (&p_prev)[4],
                                           bf16x8_t (&p_cur)[4], int t) {
-  asm volatile("" : "+v"(a.k), "+v"(a.v0), "+v"(a.v1));
-  if (t + 2 < x.n_tiles) dma(x, x.kbase, t + 2, kKFill);
-  dma(x, x.vbase, t, kVFill);
+  asm volatile("" : "+v"(a.k), "+v"(a.v));
+  dma_k(x, t + 3, ring(t));
+  dma_vt(x, t + 1, ring(t + 1));
+  const Addr b = at_buffers(a, ring(t + 1), kVRing + ring(t + 2));
 
   const float c = x.c, mc = st.m * c;
-  float ps[4] = {0.f, 0.f, 0.f, 0.f};
+  float psum;
   s_next[0] = f32x16_t{};
   s_next[1] = f32x16_t{};
   if (kPV) {
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float xa[16], xb[16];
+    float xs[32];
+    uint32_t w[16];
+    float hi, lo;
     bf16x8_t op[32];
-    op[0] = slot_operand<kKNext, kVPrev>(0, x.lds, a);
-    op[1] = slot_operand<kKNext, kVPrev>(1, x.lds, a);
+    op[0] = slot_operand(0, x.lds, b);
+    op[1] = slot_operand(1, x.lds, b);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      if (k + 2 < 32) op[k + 2] = slot_operand<kKNext, kVPrev>(k + 2, x.lds, a);
-      const int i = k >> 1;
-      if ((k & 1) == 0) {
-        s_next[i & 1] = mfma32(op[k], st.q[i >> 1], s_next[i & 1]);
-      } else {
-        st.o[i & 3] = mfma32(op[k], p_prev[i >> 2], st.o[i & 3]);
-      }
-      const int kb = i >> 3, e = 2 * (i & 7);  // score pair i = k/2
-      if ((k & 1) == 0) {
-        xa[i] = fmaf(s_cur[kb][e], c, -mc);
-        xb[i] = fmaf(s_cur[kb][e + 1], c, -mc);
-        if (i > 0) {
-          const int kb1 = (i - 1) >> 3, e1 = 2 * ((i - 1) & 7);
-          bf16x2_t pr;
-          pr[0] = (__bf16)xa[i - 1];
-          pr[1] = (__bf16)xb[i - 1];
-          ps[(i - 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps[(i - 1) & 3], false);
-          p_cur[2 * kb1 + (e1 >> 3)][e1 & 7] = pr[0];
-          p_cur[2 * kb1 + (e1 >> 3)][(e1 & 7) + 1] = pr[1];
+    for (int k = 0; k < 36; ++k) {
+      if (k < 32) {
+        if (k + 2 < 32) op[k + 2] = slot_operand(k + 2, x.lds, b);
+        const int i = k >> 1;
+        if ((k & 1) == 0) {
+          s_next[i & 1] = mfma32(op[k], st.q[i >> 1], s_next[i & 1]);
+        } else {
+          st.o[i & 3] = mfma32(op[k], p_prev[i >> 2], st.o[i & 3]);
         }
-      } else {
-        xa[i] = __builtin_amdgcn_exp2f(xa[i]);
-        xb[i] = __builtin_amdgcn_exp2f(xb[i]);
+        xs[k] = fmaf(s_cur[k >> 4][k & 15], c, -mc);
       }
+      if (k >= 1 && k <= 32) xs[k - 1] = __builtin_amdgcn_exp2f(xs[k - 1]);
+      if ((k & 1) == 1 && k >= 3) {
+        const int i = (k - 3) >> 1;
+        w[i] = pack_bf16x2(xs[2 * i], xs[2 * i + 1]);
+        // Opaque: the sums below must read the packed pair, not a second
+        // conversion of one of its halves.
+        asm volatile("" : "+v"(w[i]));
+      }
+      if (k == 4) hi = hi_bf16(w[0]);
+      if ((k & 1) == 0 && k >= 6) hi += hi_bf16(w[(k - 4) >> 1]);
+      if (k == 5) lo = lo_bf16(w[0]);
+      if ((k & 1) == 1 && k >= 7) lo += lo_bf16(w[(k - 5) >> 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    bf16x2_t pr;
-    pr[0] = (__bf16)xa[15];
-    pr[1] = (__bf16)xb[15];
-    ps[3] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps[3], false);
-    p_cur[3][6] = pr[0];
-    p_cur[3][7] = pr[1];
+    store_pairs(w, p_cur);
+    psum = hi + lo;
   } else {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        s_next[kb] = mfma32(slot_operand<kKNext, kVPrev>(4 * ks + 2 * kb, x.lds, a), st.q[ks], s_next[kb]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) weight_pair(s_cur, i, c, mc, p_cur, ps);
+      for (int kb = 0; kb < 2; ++kb) s_next[kb] = mfma32(k_operand(kb, ks, x.lds, b), st.q[ks], s_next[kb]);
+    psum = weights(s_cur, c, mc, p_cur);
   }
-  float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
   if (__builtin_amdgcn_ballot_w64(!(psum <= kSumBound)) != 0) {
     cold_path();
     psum = rebase(s_cur, st, c, p_cur);
@@ -399,14 +439,14 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     cold_path();
     mask_tail(s_next, (t + 1) * kBN, x.L, x.g);
   }
-  dma_wait();
-  __syncthreads();  // K(t+2), V(t) landed; every wave is done with K(t+1), V(t-1)
+  dma_wait_all_but<2 * kDmaPerWave>();  // this iteration's DMA may still be in flight
+  __syncthreads();  // K(t+2), V^T(t) landed; every wave is done with K(t+1), V^T(t-1)
 }
 
-__global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, int L, int H, float scale_log2e, int n_qtiles) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[4 * kTileBytes];
+__global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
+    uint16_t* __restrict__ out, int L, int H, int Lp, float scale_log2e, int n_qtiles) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStages * kTileBytes];
 
   // Workgroups are dispatched round-robin over the 8 XCDs (block b -> XCD b%8).
   // Renumber so each XCD receives a contiguous run of (head, q-tile) work:
@@ -429,25 +469,25 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
   x.L = L;
   x.c = scale_log2e;
   const int64_t tok_stride = (int64_t)H * kD;      // elements between consecutive tokens
+  const int64_t vt_row_bytes = (int64_t)Lp * 2;    // one channel row of V^T
   x.row_bytes = tok_stride * 2;
   x.n_full = L / kBN;                              // tiles with 64 real keys
   x.n_tiles = (L + kBN - 1) / kBN;                 // plus one partial tile if L % 64 != 0
-  x.tile_stride_bytes = (int64_t)kBN * x.row_bytes;
+  x.k_tile_bytes = (int64_t)kBN * x.row_bytes;
   x.kbase = reinterpret_cast<const char*>(k + (int64_t)head * kD);
-  x.vbase = reinterpret_cast<const char*>(v + (int64_t)head * kD);
-  x.dma = dma_offsets(tok_stride, x.wave, lane);
+  x.vtbase = reinterpret_cast<const char*>(vt + (int64_t)head * kD * Lp);
+  x.vt_valid = (kD - 1) * vt_row_bytes + kBN * 2;
+  x.kdma = k_dma_offsets(tok_stride, x.wave, lane);
+  x.vdma = vt_dma_offsets(vt_row_bytes, x.wave, lane);
 
   Addr a;
   a.k = 256u * col + ((16u * x.g) ^ (16u * swz(col)));
-  {
-    const int key_a = 4 * (lane >> 5) + ((lane & 15) >> 2);  // transposed-read key of this lane
-    const int ch = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // transposed-read channel
-    a.v0 = 256u * key_a + 8u * ((ch >> 2) & 1) + ((16u * (ch >> 3)) ^ (16u * swz(key_a)));
-    a.v1 = 256u * (8 + key_a) + 8u * ((ch >> 2) & 1) + ((16u * (ch >> 3)) ^ (16u * swz(8 + key_a)));
-  }
+  a.v = 128u * col + 16u * (x.g ^ vswz(col));
 
-  dma(x, x.kbase, 0, kK0);
-  if (x.n_tiles > 1) dma(x, x.kbase, 1, kK1);
+  // Ring fill: K(0), K(1), K(2) and V^T(0).
+#pragma unroll
+  for (int i = 0; i < kStages; ++i) dma_k(x, i, ring(i));
+  dma_vt(x, 0, ring(0));
 
   // Q^T operand: lane holds Q[row][16ks + 8g .. +7] for its query row.
   State st;
@@ -465,38 +505,41 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
   st.m = -FLT_MAX;
   st.l = 0.f;
   dma_wait();
-  __syncthreads();  // K(0), K(1) are in LDS
+  __syncthreads();  // the ring fill is in LDS
 
   f32x16_t s0[2], s1[2];
   bf16x8_t p0[4], p1[4];
   s0[0] = f32x16_t{};
   s0[1] = f32x16_t{};
+  {
+    const Addr b0 = at_buffers(a, ring(0), kVRing);
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    qk_step<kK0>(s0[0], 0, ks, st, x.lds, a);
-    qk_step<kK0>(s0[1], 1, ks, st, x.lds, a);
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s0[kb] = mfma32(k_operand(kb, ks, x.lds, b0), st.q[ks], s0[kb]);
   }
   if (x.n_full == 0) mask_tail(s0, 0, L, x.g);
-  // The first iteration refills buffer K0 with K(2): every wave must be done
+  // The first iteration refills K(0)'s slot with K(3): every wave must be done
   // reading K(0) first.  (Later refills are ordered by the previous
   // iteration's barrier.)
   __syncthreads();
 
-  // Iteration t reads K(t+1) from buffer (t+1)%2 and V(t-1) from buffer
-  // (t-1)%2; S(t) and P(t) live in s/p[t%2].  Odd/even pairs keep the buffer
-  // choice static.
-  iteration<kK1, kV1, kK0, kV0, false>(x, st, a, s0, s1, p1, p0, 0);
+  // S(t) and P(t) live in s/p[t % 2]; odd/even pairs keep that choice static.
+  iteration<false>(x, st, a, s0, s1, p1, p0, 0);
   int t = 1;
   for (; t + 1 < x.n_tiles; t += 2) {
-    iteration<kK0, kV0, kK1, kV1, true>(x, st, a, s1, s0, p0, p1, t);
-    iteration<kK1, kV1, kK0, kV0, true>(x, st, a, s0, s1, p1, p0, t + 1);
+    iteration<true>(x, st, a, s1, s0, p0, p1, t);
+    iteration<true>(x, st, a, s0, s1, p1, p0, t + 1);
   }
+  // P(n-1) V(n-1); V^T(n-1) landed before the last iteration's barrier.
+  const Addr b_last = at_buffers(a, 0, kVRing + ring(x.n_tiles - 1));
   if (t < x.n_tiles) {
-    iteration<kK0, kV0, kK1, kV1, true>(x, st, a, s1, s0, p0, p1, t);
-    pv<kV1>(st, p1, x.lds, a);  // P(t) V(t), t odd
+    iteration<true>(x, st, a, s1, s0, p0, p1, t);
+    pv(st, p1, x.lds, b_last);
   } else {
-    pv<kV0>(st, p0, x.lds, a);  // P(t-1) V(t-1), t-1 even
+    pv(st, p0, x.lds, b_last);
   }
+  dma_wait();  // the refetches past the end, before the workgroup exits
 
   // Epilogue: full row sum = both lane-halves; O / l -> bf16.
   const float inv_l = 1.0f / pair_sum(st.l);
@@ -514,17 +557,68 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
   }
 }
 
+// ---------------------------------------------------------------- V transpose
+// vt[h][c][j] = v[j][h][c] for j < L, 0 for L <= j < Lp.  One 256-thread
+// workgroup per (64-key block, head): the block's 64 rows x 256 bytes go
+// through LDS (row stride 65 words: the column reads then hit 32 distinct
+// banks), and every 8 consecutive lanes write one 128-byte run of a V^T row.
+constexpr int kVtThreads = 256;
+
+__global__ __launch_bounds__(kVtThreads) void v_transpose_kernel(const uint16_t* __restrict__ v,
+                                                                 uint16_t* __restrict__ vt, int L, int H,
+                                                                 int Lp) {
+  __shared__ uint32_t tile[kBN * 65];
+  const int nblk = Lp / kBN;
+  const int head = blockIdx.x / nblk, key0 = (blockIdx.x - head * nblk) * kBN, tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * kVtThreads + tid, r = idx >> 4, c16 = idx & 15;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (key0 + r < L)
+      val = *reinterpret_cast<const uint4*>(v + ((int64_t)(key0 + r) * H + head) * kD + 8 * c16);
+    uint32_t* dst = tile + r * 65 + 4 * c16;
+    dst[0] = val.x;
+    dst[1] = val.y;
+    dst[2] = val.z;
+    dst[3] = val.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * kVtThreads + tid, d = idx >> 3, c = idx & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = tile[(8 * c + 2 * e) * 65 + (d >> 1)];
+      const uint32_t hi = tile[(8 * c + 2 * e + 1) * 65 + (d >> 1)];
+      w[e] = (d & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    *reinterpret_cast<uint4*>(vt + ((int64_t)head * kD + d) * Lp + key0 + 8 * c) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 }  // namespace
 
+int64_t attention_padded_length(int64_t L) { return (L + kBN - 1) / kBN * kBN; }
+int64_t attention_workspace_bytes(int64_t L, int32_t H) { return (int64_t)H * kD * attention_padded_length(L) * 2; }
 int64_t attention_grid_blocks(int64_t L, int32_t H) { return ((L + kBM - 1) / kBM) * (int64_t)H; }
+int attention_block_threads() { return kThreads; }
+int64_t transpose_grid_blocks(int64_t L, int32_t H) { return attention_padded_length(L) / kBN * (int64_t)H; }
+int transpose_block_threads() { return kVtThreads; }
 
 hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                    uint16_t* out, int64_t L, int32_t H, float scale,
+                                    uint16_t* out, uint16_t* vt, int64_t L, int32_t H, float scale,
                                     hipStream_t stream) {
+  const int Lp = (int)attention_padded_length(L);
+  hipLaunchKernelGGL(v_transpose_kernel, dim3((unsigned)transpose_grid_blocks(L, H)), dim3(kVtThreads), 0,
+                     stream, v, vt, (int)L, (int)H, Lp);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int n_qtiles = (int)((L + kBM - 1) / kBM);
   const dim3 grid((unsigned)attention_grid_blocks(L, H));
-  hipLaunchKernelGGL(attention_fwd_kernel, grid, dim3(kThreads), 0, stream, q, k, v, out, (int)L,
-                     (int)H, scale * kLog2e, n_qtiles);
+  hipLaunchKernelGGL(attention_fwd_kernel, grid, dim3(kThreads), 0, stream, q, k, vt, out, (int)L, (int)H, Lp,
+                     scale * kLog2e, n_qtiles);
   return hipGetLastError();
 }
 
