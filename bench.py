@@ -109,8 +109,7 @@ def main() -> int:
 
     import numpy as np
     import torch
-    from packed_full_attention_amd import (h3attn_forward, h3attn_forward_workspace_bytes, h3attn_qk_prologue,
-                                           load_library)
+    from packed_full_attention_amd import h3attn_forward, h3attn_qk_prologue, load_library
     from packed_full_attention_amd import workloads as wl
 
     load_library()
@@ -123,7 +122,6 @@ def main() -> int:
     gq, gk = torch.from_numpy(inp.gamma_q).to(dev), torch.from_numpy(inp.gamma_k).to(dev)
     pos = torch.from_numpy(inp.pos).to(dev)
     out = torch.empty_like(q)
-    ws = torch.empty(h3attn_forward_workspace_bytes(L, H), dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(128.0)
 
     if args.copy_probe:
@@ -136,7 +134,7 @@ def main() -> int:
 
     def step():
         h3attn_qk_prologue(q, k, gq, gk, pos)
-        h3attn_forward(q, k, v, out, scale=scale, workspace=ws)
+        h3attn_forward(q, k, v, out, scale=scale)
 
     for _ in range(args.warmup):
         step()
@@ -153,7 +151,7 @@ def main() -> int:
         ev[i][0].record(stream)
         h3attn_qk_prologue(q, k, gq, gk, pos)
         ev[i][1].record(stream)
-        h3attn_forward(q, k, v, out, scale=scale, workspace=ws)
+        h3attn_forward(q, k, v, out, scale=scale)
         ev[i][2].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()

@@ -44,14 +44,13 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 2
+#define H3ATTN_ABI_VERSION 1
 #define H3ATTN_HEAD_DIM 128
 
 /* Status codes. */
 #define H3A_OK 0            /* success (work enqueued)                               */
 #define H3A_EINVAL 1        /* null pointer, L <= 0, H <= 0, misalignment, overlap,   */
-                            /* a non-finite / non-positive scale, or a workspace      */
-                            /* smaller than h3attn_forward_workspace_bytes            */
+                            /* or a non-finite / non-positive scale                   */
 #define H3A_EUNSUPPORTED 2  /* geometry outside the supported range (L >= 2^31,       */
                             /* grid or size overflow)                                 */
 #define H3A_EHIP 3          /* the HIP launch reported an error                       */
@@ -82,21 +81,11 @@ int h3attn_qk_prologue(void* q, void* k, const float* gamma_q, const float* gamm
                        const int32_t* pos_thw, int64_t L, int32_t H, hipStream_t stream);
 
 /*
- * Device workspace, in bytes, that h3attn_forward needs for (L, H):
- * H * 128 * Lp * 2 with Lp = L rounded up to a multiple of 64 (a transposed,
- * zero-padded bf16 copy of v).  Returns -1 for an (L, H) that h3attn_forward
- * would reject as L <= 0, H <= 0, L >= 2^31 or too large.
- */
-int64_t h3attn_forward_workspace_bytes(int64_t L, int32_t H);
-
-/*
  * Full bidirectional attention, per head h, over all L tokens with no mask:
  *   out[i,h,:] = sum_j softmax_j( scale * <q[i,h,:], k[j,h,:]> ) * v[j,h,:]
  * S = Q K^T and P V on bf16 matrix cores with fp32 accumulation; online
  * softmax in fp32 (P rounded to bf16 as the P V operand); the output is
  * divided by the fp32 row sum and rounded to bf16 (round to nearest even).
- * Two kernels are enqueued: v is first copied, transposed per head, into the
- * workspace, then the attention kernel reads q, k and that copy.
  *
  *   q, k, v  bf16 [L][H][128] inputs (q and k normally come from
  *            h3attn_qk_prologue; v is used as given); 16-byte aligned; they
@@ -105,17 +94,9 @@ int64_t h3attn_forward_workspace_bytes(int64_t L, int32_t H);
  *            or v.
  *   L, H     as above.
  *   scale    softmax scale, finite and > 0 (1/sqrt(128) for the H3 block).
- *   workspace, workspace_bytes
- *            caller-owned device scratch of at least
- *            h3attn_forward_workspace_bytes(L, H) bytes, 16-byte aligned, not
- *            overlapping q, k, v or out.  Its contents on entry do not matter
- *            and are overwritten; it may be reused as soon as the call's work
- *            on `stream` has finished.  Calls in flight at the same time (on
- *            different streams) need separate workspaces.
  */
 int h3attn_forward(const void* q, const void* k, const void* v, void* out, int64_t L,
-                   int32_t H, float scale, void* workspace, int64_t workspace_bytes,
-                   hipStream_t stream);
+                   int32_t H, float scale, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* h3attn_strerror(int status);

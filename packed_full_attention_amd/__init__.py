@@ -1,14 +1,12 @@
 """MI355X-native packed full attention for the MiniMax-H3 block.
 
 The product is libh3attn.so (C ABI declared in include/h3attn.h): a fused Q/K
-RMSNorm + MM-RoPE prologue and the attention forward (a V transpose into a
-caller workspace, then the flash-attention kernel), all hand-written HIP for
-gfx950.  This package holds the build script, the thin
+RMSNorm + MM-RoPE prologue and a flash-attention forward kernel, both
+hand-written HIP for gfx950.  This package holds the build script, the thin
 ctypes binding with the same names as the C entry points, and the seeded
 synthetic workloads.
 """
-from ._binding import (H3AttnError, abi_version, h3attn_forward, h3attn_forward_workspace_bytes,  # noqa: F401
-                       h3attn_qk_prologue, load_library, LIB_PATH)
+from ._binding import (H3AttnError, abi_version, h3attn_forward, h3attn_qk_prologue,  # noqa: F401
+                       load_library, LIB_PATH)
 
-__all__ = ["h3attn_qk_prologue", "h3attn_forward_workspace_bytes", "h3attn_forward", "abi_version",
-           "load_library", "H3AttnError"]
+__all__ = ["h3attn_qk_prologue", "h3attn_forward", "abi_version", "load_library", "H3AttnError"]

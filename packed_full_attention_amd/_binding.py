@@ -17,8 +17,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libh3attn.so")
 HEAD_DIM = 128
 H3A_OK, H3A_EINVAL, H3A_EUNSUPPORTED, H3A_EHIP = 0, 1, 2, 3
-EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward_workspace_bytes", "h3attn_forward",
-                    "h3attn_strerror", "h3attn_last_error", "h3attn_abi_version")
+EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward", "h3attn_strerror",
+                    "h3attn_last_error", "h3attn_abi_version")
 
 _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
@@ -43,9 +43,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         lib.h3attn_qk_prologue.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp]
         lib.h3attn_qk_prologue.restype = ctypes.c_int
-        lib.h3attn_forward_workspace_bytes.argtypes = [i64, i32]
-        lib.h3attn_forward_workspace_bytes.restype = i64
-        lib.h3attn_forward.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, vp, i64, vp]
+        lib.h3attn_forward.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, vp]
         lib.h3attn_forward.restype = ctypes.c_int
         lib.h3attn_strerror.argtypes = [ctypes.c_int]
         lib.h3attn_strerror.restype = ctypes.c_char_p
@@ -105,18 +103,8 @@ def h3attn_qk_prologue(q, k, gamma_q, gamma_k, pos_thw) -> None:
     _raise_on(lib, "h3attn_qk_prologue", st)
 
 
-def h3attn_forward_workspace_bytes(L: int, H: int) -> int:
-    """Bytes of device workspace h3attn_forward needs for (L, H); -1 if (L, H) is rejected."""
-    return int(load_library().h3attn_forward_workspace_bytes(int(L), int(H)))
-
-
-def h3attn_forward(q, k, v, out=None, scale: Optional[float] = None, workspace=None):
-    """Full bidirectional attention on bf16 [L, H, 128]; returns out (see include/h3attn.h).
-
-    workspace: a uint8 GPU tensor of at least h3attn_forward_workspace_bytes(L, H)
-    bytes; when omitted, one is allocated for this call (it must outlive the
-    call's GPU work, which torch's caching allocator guarantees on this stream).
-    """
+def h3attn_forward(q, k, v, out=None, scale: Optional[float] = None):
+    """Full bidirectional attention on bf16 [L, H, 128]; returns out (see include/h3attn.h)."""
     import torch
     L, H = _lh(q)
     dev = q.device
@@ -129,14 +117,10 @@ def h3attn_forward(q, k, v, out=None, scale: Optional[float] = None, workspace=N
     if scale is None:
         scale = 1.0 / math.sqrt(HEAD_DIM)
     lib = load_library()
-    need = int(lib.h3attn_forward_workspace_bytes(L, H))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    _check_tensor("workspace", workspace, torch.uint8, (workspace.numel(),), dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.h3attn_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), L, H,
-                                float(scale), workspace.data_ptr(), workspace.numel(), stream)
+                                float(scale), stream)
     _raise_on(lib, "h3attn_forward", st)
     return out
 

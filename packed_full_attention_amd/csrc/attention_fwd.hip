@@ -10,15 +10,6 @@
 // atomics; every output row is produced by exactly one wave, so the result
 // does not depend on the grid or on the number of CUs.
 //
-// Two launches.  v_transpose_kernel writes V^T, [H][128][Lp] with Lp = L
-// rounded up to 64 and zeros past L, into the caller's workspace; the
-// attention kernel then reads K from [L][H][128] and V^T from the workspace.
-// The transposed copy lets every P*V operand be one 16-byte LDS read: the
-// transposing LDS read (ds_read_b64_tr_b16) that would otherwise build the
-// operand from row-major V moves a quarter of the bytes per cycle that
-// ds_read_b128 does on gfx950, and with it the LDS, not the matrix cores,
-// bounded the kernel.  The copy costs one extra HBM pass over V.
-//
 // Work decomposition.  A 512-thread workgroup owns BM = 256 query rows of one
 // head; each of its 8 waves owns 32 of them (two waves per SIMD, one workgroup
 // per CU).  Keys stream through LDS in tiles of BN = 64, shared by all 8
@@ -34,11 +25,9 @@
 //
 // Key order.  The B operand of a 32x32x16 MFMA takes k-slots 8g .. 8g+7 from
 // lane half g; the P^T operand built from S^T accumulator rows holds, in those
-// slots, tile rows 16j + {4g .. 4g+3, 8+4g .. 11+4g}.  The V^T operand read as
-// one 16-byte chunk holds keys 16j + 8g .. 16j + 8g + 7.  The two agree because
-// the K tile is stored with its rows permuted: LDS row r of a K tile holds key
-// perm(r), perm swapping bits 2 and 3 of r (an involution within each group of
-// 16 keys).
+// slots, keys 16j + {4g .. 4g+3, 8+4g .. 11+4g}.  The V^T operand is gathered
+// from the row-major V tile in that same key order by two transposing LDS
+// reads (ds_read_b64_tr_b16), so no data is reordered anywhere.
 //
 // Software pipeline.  Iteration t issues
 //   S(t+1) = K(t+1) Q^T        (matrix cores)
@@ -49,22 +38,21 @@
 // instruction runs for 32 cycles, during which the same SIMD executes about
 // three independent VALU instructions of this or of the other wave at no cost.
 //
-// LDS.  Two rings of three 16 KiB tiles, K and V^T: during iteration t the
-// waves read K(t+1) and V^T(t-1) while DMA (buffer_load_dwordx4 ... lds, no
-// VGPR staging) fills K(t+3) and V^T(t+1), each into the slot its ring freed
-// in iteration t-1; one barrier per tile, and a DMA has two iterations to land.
+// LDS.  Two rings of three 16 KiB tiles, K and V: during iteration t the
+// waves read K(t+1) and V(t-1) while DMA (buffer_load_dwordx4 ... lds, no
+// VGPR staging) fills K(t+3) and V(t+1), each into the slot its ring freed in
+// iteration t-1; one barrier per tile, and a DMA has two iterations to land.
 // The DMA is issued by inline asm and awaited explicitly (vmcnt) before each
 // tile barrier: the compiler, which cannot prove that the in-flight writes miss
 // the buffers being read, would otherwise wait for them before every LDS read.
-// Layouts (64 four-byte banks; a 16-byte read serves 16 lanes per cycle, so
-// each group of 16 lanes must cover all 64 banks):
-//   K tile: 64 rows x 256 bytes (sixteen 16-byte chunks), chunk c of row r at
-//     physical chunk c ^ swz(r), swz(r) = 4 (r & 3) + ((r >> 2) & 3), which
-//     takes 16 distinct values over any 16 consecutive rows (the K operand
-//     read: 16 lanes = 16 rows, one chunk);
-//   V^T tile: 128 rows (channels) x 128 bytes (eight chunks of 8 keys), chunk
-//     c of row d at physical chunk c ^ ((d >> 1) & 7): 16 consecutive rows then
-//     fill 16 distinct 16-byte bank groups.
+// Both tiles are stored row-major (one 256-byte row per key, sixteen 16-byte
+// chunks), chunk c of row r at physical chunk c ^ swz(r),
+// swz(r) = 4 (r & 3) + ((r >> 2) & 3).  The LDS has 64 four-byte banks and
+// serves 16 lanes of a 16-byte read, or 32 lanes of an 8-byte read, per cycle;
+// swz takes 16 distinct values over any 16 consecutive rows (the K operand
+// read) and distinct top bits over 4 consecutive rows (the transposing V read:
+// 32 lanes = 4 keys x 4 chunks), so both are conflict-free (checked with the
+// SQ_LDS_BANK_CONFLICT counter).
 //
 // Exponent offset.  The weights of a tile are computed against the offset m
 // the row already has, with no per-tile maximum.  Each lane adds up the bf16
@@ -88,7 +76,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 
 constexpr int kD = 128;
@@ -97,9 +87,10 @@ constexpr int kBM = 32 * kWaves;          // query rows per workgroup
 constexpr int kBN = 64;                   // keys per tile
 constexpr int kThreads = 64 * kWaves;
 constexpr int kDmaPerWave = 16 / kWaves;  // 1 KiB DMA pieces per wave per tile
-constexpr int kTileBytes = kBN * kD * 2;  // 16 KiB per K or V^T tile
+static_assert(kDmaPerWave == 2, "the slot loop issues two K and two V pieces per wave");
+constexpr int kTileBytes = kBN * kD * 2;  // 16 KiB per K or V tile
 constexpr int kStages = 3;                // tiles per ring (resident or in flight)
-constexpr int kVRing = kStages * kTileBytes;  // the V^T ring follows the K ring
+constexpr int kVRing = kStages * kTileBytes;  // the V ring follows the K ring
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSumBound = 256.0f;        // a lane's tile sum of P above this moves the offset
 
@@ -126,67 +117,66 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
-// Key held by row r of a K tile (and by S^T accumulator row r).
-__device__ __forceinline__ int perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 // ---------------------------------------------------------------- tile DMA
-// A 16 KiB tile goes into LDS as 16 pieces of 1 KiB; wave w writes pieces w and
-// w+8.  A piece is 64 lanes x 16 bytes in lane order at M0; each lane fetches
-// the global chunk that belongs at its slot, at a fixed byte offset from the
-// tile base.  Loads go through a buffer resource whose size ends at the last
-// valid byte: K rows past the document read as zeros (their scores are masked
-// to -inf), and no address outside the tensors is used.
+// A 64-key tile of a [L][H][128] tensor goes into LDS as 16 pieces of 1 KiB;
+// wave w writes pieces w and w+8.  A piece is 64 lanes x 16 bytes in lane order
+// at M0; each lane fetches the global chunk that belongs at its slot, at a fixed
+// byte offset from the tile base.  Loads go through a buffer resource whose size
+// ends at the document's last row: rows past it read as zeros (their scores are
+// masked to -inf and their V rows then contribute nothing), and no address
+// outside the tensor is used.
 constexpr int kBufferDword3 = 0x00020000;  // raw buffer, 32-bit data format
 
 struct DmaOffsets {
   uint32_t off[kDmaPerWave];
 };
 
-// K tile: slot (row r, physical chunk p) <- key perm(r), channels 8 (p ^ swz(r)) .. +7.
-__device__ __forceinline__ DmaOffsets k_dma_offsets(int64_t tok_stride, int wave, int lane) {
+// Slot (row r, physical chunk p) <- token r of the tile, channels 8 (p ^ swz(r)) .. +7.
+__device__ __forceinline__ DmaOffsets dma_offsets(int64_t tok_stride, int wave, int lane) {
   DmaOffsets d;
 #pragma unroll
   for (int it = 0; it < kDmaPerWave; ++it) {
     const int slot = (it * kWaves + wave) * 64 + lane;  // 16-byte slot in the tile
     const int r = slot >> 4;
     const int c = (slot & 15) ^ swz(r);
-    d.off[it] = (uint32_t)(((int64_t)perm(r) * tok_stride + 8 * c) * 2);
+    d.off[it] = (uint32_t)(((int64_t)r * tok_stride + 8 * c) * 2);
   }
   return d;
 }
 
-// V^T tile: slot (row d, physical chunk p) <- channel d, keys 8 (p ^ vswz(d)) .. +7.
-__device__ __forceinline__ DmaOffsets vt_dma_offsets(int64_t vt_row_bytes, int wave, int lane) {
-  DmaOffsets d;
-#pragma unroll
-  for (int it = 0; it < kDmaPerWave; ++it) {
-    const int slot = (it * kWaves + wave) * 64 + lane;
-    const int r = slot >> 3;
-    const int c = (slot & 7) ^ vswz(r);
-    d.off[it] = (uint32_t)(r * vt_row_bytes + 16 * c);
-  }
-  return d;
-}
+// A tile's DMA: the buffer resource (tile_base: first byte of the tile;
+// valid_bytes: bytes from there to the end of the valid data) and this wave's
+// LDS destination (the tile's LDS offset plus its first piece).
+struct TileDma {
+  i32x4_t rsrc;
+  uint32_t lds;
+};
 
-// tile_base: first byte of the tile; valid_bytes: bytes from there to the end
-// of the valid data.
-__device__ __forceinline__ void tile_dma(const char* tile_base, int64_t valid_bytes, const DmaOffsets& d,
-                                         uint32_t lds_tile, int wave) {
+__device__ __forceinline__ TileDma tile_dma(const char* tile_base, int64_t valid_bytes, uint32_t lds_tile,
+                                            int wave) {
   const uint64_t b = (uint64_t)(uintptr_t)tile_base;
   const uint32_t n = valid_bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)valid_bytes;
-  const i32x4_t rsrc = {(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
-                        (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)),
-                        (int)__builtin_amdgcn_readfirstlane(n), kBufferDword3};
+  TileDma t;
+  t.rsrc = i32x4_t{(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
+                   (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)),
+                   (int)__builtin_amdgcn_readfirstlane(n), kBufferDword3};
+  t.lds = __builtin_amdgcn_readfirstlane(lds_tile + wave * 1024);
+  return t;
+}
+
+// Issue this wave's DMA piece it (0 .. kDmaPerWave-1) of a tile.
+__device__ __forceinline__ void dma_piece(const TileDma& t, const DmaOffsets& d, int it) {
+  // One wait state between writing M0 and the LDS-DMA instruction that reads it.
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :
+               : "v"(d.off[it]), "s"(t.lds + it * kWaves * 1024), "s"(t.rsrc)
+               : "memory");
+}
+
+__device__ __forceinline__ void dma_all(const TileDma& t, const DmaOffsets& d) {
 #pragma unroll
-  for (int it = 0; it < kDmaPerWave; ++it) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_tile + (it * kWaves + wave) * 1024);
-    // One wait state between writing M0 and the LDS-DMA instruction that reads it.
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :
-                 : "v"(d.off[it]), "s"(m0), "s"(rsrc)
-                 : "memory");
-  }
+  for (int it = 0; it < kDmaPerWave; ++it) dma_piece(t, d, it);
 }
 
 // s_waitcnt immediate for vmcnt(n) (expcnt and lgkmcnt left at their maxima).
@@ -211,20 +201,22 @@ struct State {
   float l;         // this lane-half's partial sum of P
 };
 
-// LDS read addresses.  The k-step of a K read and the key step of a V^T read
-// enter the byte offset through bits that no other term touches, so each read
-// address is a per-lane base XOR a constant, plus an immediate:
+// LDS read addresses.  With the swizzle above, the k-step of a K read and the
+// d-block of a V read enter the byte offset through bits that no other term
+// touches, so each read address is a per-lane base XOR a constant, plus an
+// immediate for the 32-key block or the 16-key step:
 //   K (row 32 kb + col, channels 16 ks + 8 g .. +7):
 //     kb * 8192 + (kaddr ^ 32 ks),  kaddr = buf + 256 col + (16 g ^ 16 swz(col))
-//   V^T (row 32 dblk + col, keys 16 j + 8 g .. +7):
-//     dblk * 4096 + (vaddr ^ 32 j),  vaddr = buf + 128 col + 16 (g ^ vswz(col))
+//   V (row 16 j + 8 h + key_a, channels 32 dblk + ch .. +3):
+//     4096 j + (vaddr[h] ^ 64 dblk),
+//     vaddr[h] = buf + 256 (8 h + key_a) + 8 ((ch >> 2) & 1) + (16 (ch >> 3) ^ 16 swz(8 h + key_a))
 // The buffer offset buf is a multiple of 16 KiB and does not meet the XOR.
 struct Addr {
-  uint32_t k, v;
+  uint32_t k, v0, v1;
 };
 
 __device__ __forceinline__ Addr at_buffers(const Addr& a, uint32_t kbuf, uint32_t vbuf) {
-  return Addr{a.k + kbuf, a.v + vbuf};
+  return Addr{a.k + kbuf, a.v0 + vbuf, a.v1 + vbuf};
 }
 
 // Operand of the score MFMA for 32-key block kb, k-step ks.
@@ -232,9 +224,18 @@ __device__ __forceinline__ bf16x8_t k_operand(int kb, int ks, const lds_char* ld
   return *(const lds_bf16x8*)(lds + kb * 8192 + (b.k ^ (32u * ks)));
 }
 
-// Operand of the P*V MFMA for d-block dblk, 16-key step j.
+// Operand of the P*V MFMA for d-block dblk, 16-key step j: two transposing
+// reads.  Lane l (group G = l >> 4, index i = l & 15) addresses key
+// 16 j + 4 (G >> 1) + (i >> 2) (+8 for the second read) at channel
+// 32 dblk + 16 (G & 1) + 4 (i & 3), and receives keys {16 j + 4 g + e} and
+// {16 j + 8 + 4 g + e} of channel 32 dblk + (l % 32) -- the key order of the
+// P^T accumulator slots.
 __device__ __forceinline__ bf16x8_t v_operand(int dblk, int j, const lds_char* lds, const Addr& b) {
-  return *(const lds_bf16x8*)(lds + dblk * 4096 + (b.v ^ (32u * j)));
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(lds + 4096 * j + (b.v0 ^ (64u * dblk))));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(lds + 4096 * j + (b.v1 ^ (64u * dblk))));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // O^T += V_tile^T P^T.
@@ -307,8 +308,7 @@ __device__ __forceinline__ float rebase(const f32x16_t (&s_in)[2], State& st, fl
 }
 
 // Scores of keys at or past L (only in the last, partial tile) become -inf.
-// Accumulator slot 4r + qq of lane half g is tile row 32 kb + 8 r + 4 g + qq,
-// which holds key perm(row).
+// Accumulator slot 4r + qq of lane half g is key 32 kb + 8 r + 4 g + qq.
 __device__ __forceinline__ void mask_tail(f32x16_t (&s)[2], int kbase, int L, int g) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -316,7 +316,7 @@ __device__ __forceinline__ void mask_tail(f32x16_t (&s)[2], int kbase, int L, in
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
-        if (kbase + perm(32 * kb + 8 * r + 4 * g + qq) >= L) s[kb][4 * r + qq] = -INFINITY;
+        if (kbase + 32 * kb + 8 * r + 4 * g + qq >= L) s[kb][4 * r + qq] = -INFINITY;
 }
 
 // ---------------------------------------------------------------- kernel
@@ -324,26 +324,21 @@ struct Ctx {
   const lds_char* lds;
   uint32_t lds_base;
   const char* kbase;          // K, this head, token 0
-  const char* vtbase;         // V^T, this head, channel 0, key 0
-  int64_t k_tile_bytes;       // 64 tokens of K
+  const char* vbase;          // V, this head, token 0
+  int64_t tile_bytes;         // 64 tokens of K or V
   int64_t row_bytes;          // one token row of all heads
-  int64_t vt_valid;           // bytes from a V^T tile's first byte to its last
-  DmaOffsets kdma, vdma;
+  DmaOffsets dma;
   int n_full, n_tiles, L, wave, g;
   float c;
 };
 
 // DMA of tile t (clamped to the last tile: the refetch past the end keeps the
-// number of DMA instructions per iteration fixed) into the LDS buffer at
-// byte offset buf of the K or V^T ring.
-__device__ __forceinline__ void dma_k(const Ctx& x, int t, uint32_t buf) {
+// number of DMA instructions per iteration fixed) of the tensor at base into
+// the LDS buffer at byte offset buf.
+__device__ __forceinline__ TileDma dma_tile(const Ctx& x, const char* base, int t, uint32_t buf) {
   t = t < x.n_tiles ? t : x.n_tiles - 1;
   const int64_t valid = (int64_t)(x.L - 1 - t * kBN) * x.row_bytes + kD * 2;
-  tile_dma(x.kbase + t * x.k_tile_bytes, valid, x.kdma, x.lds_base + buf, x.wave);
-}
-__device__ __forceinline__ void dma_vt(const Ctx& x, int t, uint32_t buf) {
-  t = t < x.n_tiles ? t : x.n_tiles - 1;
-  tile_dma(x.vtbase + t * (kBN * 2), x.vt_valid, x.vdma, x.lds_base + kVRing + buf, x.wave);
+  return tile_dma(base + t * x.tile_bytes, valid, x.lds_base + buf, x.wave);
 }
 
 __device__ __forceinline__ uint32_t ring(int t) { return (uint32_t)(t % kStages) * kTileBytes; }
@@ -359,10 +354,10 @@ __device__ __forceinline__ bf16x8_t slot_operand(int k, const lds_char* lds, con
 
 // Iteration t: S(t+1) from K(t+1) into s_next; O += V(t-1) P(t-1) (skipped for
 // t = 0); P(t) from s_cur into p_cur.  K(t+1) sits in ring slot (t+1) % 3 and
-// V^T(t-1) in slot (t-1) % 3.  DMA fills K(t+3) into the K slot of K(t) (read
-// in iteration t-1) and V^T(t+1) into the V slot of V^T(t-2) (read in
-// iteration t-1); the previous iteration's DMA (K(t+2), V^T(t)) must have
-// landed before the barrier that ends this one.  In the last iteration there
+// V(t-1) in slot (t-1) % 3.  DMA fills K(t+3) into the K slot of K(t) (read in
+// iteration t-1) and V(t+1) into the V slot of V(t-2) (read in iteration t-1);
+// the previous iteration's DMA (K(t+2), V(t)) must have landed before the
+// barrier that ends this one.  In the last iteration there
 // is no K(t+1): S(t+1) is computed from a stale slot and never used.
 //
 // With the P*V product (t > 0) the instruction order is fixed by hand, slot by
@@ -378,9 +373,9 @@ template <bool kPV>
 __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, const f32x16_t (&s_cur)[2],
                                           f32x16_t (&s_next)[2], const bf16x8_t (&p_prev)[4],
                                           bf16x8_t (&p_cur)[4], int t) {
-  asm volatile("" : "+v"(a.k), "+v"(a.v));
-  dma_k(x, t + 3, ring(t));
-  dma_vt(x, t + 1, ring(t + 1));
+  asm volatile("" : "+v"(a.k), "+v"(a.v0), "+v"(a.v1));
+  const TileDma kd = dma_tile(x, x.kbase, t + 3, ring(t));
+  const TileDma vd = dma_tile(x, x.vbase, t + 1, kVRing + ring(t + 1));
   const Addr b = at_buffers(a, ring(t + 1), kVRing + ring(t + 2));
 
   const float c = x.c, mc = st.m * c;
@@ -397,6 +392,13 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 36; ++k) {
+      // This iteration's DMA, one piece every 8 slots: issued all at once by
+      // all 8 waves, the loads back up in the address unit and hold the waves
+      // at the start of the iteration.
+      if (k == 4) dma_piece(kd, x.dma, 0);
+      if (k == 12) dma_piece(kd, x.dma, 1);
+      if (k == 20) dma_piece(vd, x.dma, 0);
+      if (k == 28) dma_piece(vd, x.dma, 1);
       if (k < 32) {
         if (k + 2 < 32) op[k + 2] = slot_operand(k + 2, x.lds, b);
         const int i = k >> 1;
@@ -424,6 +426,8 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     store_pairs(w, p_cur);
     psum = hi + lo;
   } else {
+    dma_all(kd, x.dma);
+    dma_all(vd, x.dma);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
@@ -440,12 +444,12 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     mask_tail(s_next, (t + 1) * kBN, x.L, x.g);
   }
   dma_wait_all_but<2 * kDmaPerWave>();  // this iteration's DMA may still be in flight
-  __syncthreads();  // K(t+2), V^T(t) landed; every wave is done with K(t+1), V^T(t-1)
+  __syncthreads();  // K(t+2), V(t) landed; every wave is done with K(t+1), V(t-1)
 }
 
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
-    uint16_t* __restrict__ out, int L, int H, int Lp, float scale_log2e, int n_qtiles) {
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ out, int L, int H, float scale_log2e, int n_qtiles) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStages * kTileBytes];
 
   // Workgroups are dispatched round-robin over the 8 XCDs (block b -> XCD b%8).
@@ -469,25 +473,27 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   x.L = L;
   x.c = scale_log2e;
   const int64_t tok_stride = (int64_t)H * kD;      // elements between consecutive tokens
-  const int64_t vt_row_bytes = (int64_t)Lp * 2;    // one channel row of V^T
   x.row_bytes = tok_stride * 2;
   x.n_full = L / kBN;                              // tiles with 64 real keys
   x.n_tiles = (L + kBN - 1) / kBN;                 // plus one partial tile if L % 64 != 0
-  x.k_tile_bytes = (int64_t)kBN * x.row_bytes;
+  x.tile_bytes = (int64_t)kBN * x.row_bytes;
   x.kbase = reinterpret_cast<const char*>(k + (int64_t)head * kD);
-  x.vtbase = reinterpret_cast<const char*>(vt + (int64_t)head * kD * Lp);
-  x.vt_valid = (kD - 1) * vt_row_bytes + kBN * 2;
-  x.kdma = k_dma_offsets(tok_stride, x.wave, lane);
-  x.vdma = vt_dma_offsets(vt_row_bytes, x.wave, lane);
+  x.vbase = reinterpret_cast<const char*>(v + (int64_t)head * kD);
+  x.dma = dma_offsets(tok_stride, x.wave, lane);
 
   Addr a;
   a.k = 256u * col + ((16u * x.g) ^ (16u * swz(col)));
-  a.v = 128u * col + 16u * (x.g ^ vswz(col));
+  {
+    const int key_a = 4 * (lane >> 5) + ((lane & 15) >> 2);  // transposing-read key of this lane
+    const int ch = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // transposing-read channel
+    a.v0 = 256u * key_a + 8u * ((ch >> 2) & 1) + ((16u * (ch >> 3)) ^ (16u * swz(key_a)));
+    a.v1 = 256u * (8 + key_a) + 8u * ((ch >> 2) & 1) + ((16u * (ch >> 3)) ^ (16u * swz(8 + key_a)));
+  }
 
-  // Ring fill: K(0), K(1), K(2) and V^T(0).
+  // Ring fill: K(0), K(1), K(2) and V(0).
 #pragma unroll
-  for (int i = 0; i < kStages; ++i) dma_k(x, i, ring(i));
-  dma_vt(x, 0, ring(0));
+  for (int i = 0; i < kStages; ++i) dma_all(dma_tile(x, x.kbase, i, ring(i)), x.dma);
+  dma_all(dma_tile(x, x.vbase, 0, kVRing + ring(0)), x.dma);
 
   // Q^T operand: lane holds Q[row][16ks + 8g .. +7] for its query row.
   State st;
@@ -531,7 +537,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     iteration<true>(x, st, a, s1, s0, p0, p1, t);
     iteration<true>(x, st, a, s0, s1, p1, p0, t + 1);
   }
-  // P(n-1) V(n-1); V^T(n-1) landed before the last iteration's barrier.
+  // P(n-1) V(n-1); V(n-1) landed before the last iteration's barrier.
   const Addr b_last = at_buffers(a, 0, kVRing + ring(x.n_tiles - 1));
   if (t < x.n_tiles) {
     iteration<true>(x, st, a, s1, s0, p0, p1, t);
@@ -557,67 +563,16 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   }
 }
 
-// ---------------------------------------------------------------- V transpose
-// vt[h][c][j] = v[j][h][c] for j < L, 0 for L <= j < Lp.  One 256-thread
-// workgroup per (64-key block, head): the block's 64 rows x 256 bytes go
-// through LDS (row stride 65 words: the column reads then hit 32 distinct
-// banks), and every 8 consecutive lanes write one 128-byte run of a V^T row.
-constexpr int kVtThreads = 256;
-
-__global__ __launch_bounds__(kVtThreads) void v_transpose_kernel(const uint16_t* __restrict__ v,
-                                                                 uint16_t* __restrict__ vt, int L, int H,
-                                                                 int Lp) {
-  __shared__ uint32_t tile[kBN * 65];
-  const int nblk = Lp / kBN;
-  const int head = blockIdx.x / nblk, key0 = (blockIdx.x - head * nblk) * kBN, tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = i * kVtThreads + tid, r = idx >> 4, c16 = idx & 15;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (key0 + r < L)
-      val = *reinterpret_cast<const uint4*>(v + ((int64_t)(key0 + r) * H + head) * kD + 8 * c16);
-    uint32_t* dst = tile + r * 65 + 4 * c16;
-    dst[0] = val.x;
-    dst[1] = val.y;
-    dst[2] = val.z;
-    dst[3] = val.w;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = i * kVtThreads + tid, d = idx >> 3, c = idx & 7;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = tile[(8 * c + 2 * e) * 65 + (d >> 1)];
-      const uint32_t hi = tile[(8 * c + 2 * e + 1) * 65 + (d >> 1)];
-      w[e] = (d & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    *reinterpret_cast<uint4*>(vt + ((int64_t)head * kD + d) * Lp + key0 + 8 * c) =
-        make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 }  // namespace
 
-int64_t attention_padded_length(int64_t L) { return (L + kBN - 1) / kBN * kBN; }
-int64_t attention_workspace_bytes(int64_t L, int32_t H) { return (int64_t)H * kD * attention_padded_length(L) * 2; }
 int64_t attention_grid_blocks(int64_t L, int32_t H) { return ((L + kBM - 1) / kBM) * (int64_t)H; }
 int attention_block_threads() { return kThreads; }
-int64_t transpose_grid_blocks(int64_t L, int32_t H) { return attention_padded_length(L) / kBN * (int64_t)H; }
-int transpose_block_threads() { return kVtThreads; }
 
 hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                    uint16_t* out, uint16_t* vt, int64_t L, int32_t H, float scale,
-                                    hipStream_t stream) {
-  const int Lp = (int)attention_padded_length(L);
-  hipLaunchKernelGGL(v_transpose_kernel, dim3((unsigned)transpose_grid_blocks(L, H)), dim3(kVtThreads), 0,
-                     stream, v, vt, (int)L, (int)H, Lp);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                                    uint16_t* out, int64_t L, int32_t H, float scale, hipStream_t stream) {
   const int n_qtiles = (int)((L + kBM - 1) / kBM);
   const dim3 grid((unsigned)attention_grid_blocks(L, H));
-  hipLaunchKernelGGL(attention_fwd_kernel, grid, dim3(kThreads), 0, stream, q, k, vt, out, (int)L, (int)H, Lp,
+  hipLaunchKernelGGL(attention_fwd_kernel, grid, dim3(kThreads), 0, stream, q, k, v, out, (int)L, (int)H,
                      scale * kLog2e, n_qtiles);
   return hipGetLastError();
 }

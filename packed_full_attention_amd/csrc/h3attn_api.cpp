@@ -83,35 +83,21 @@ int h3attn_qk_prologue(void* q, void* k, const float* gamma_q, const float* gamm
   return ok();
 }
 
-int64_t h3attn_forward_workspace_bytes(int64_t L, int32_t H) {
-  uint64_t bytes = 0;
-  if (check_shape(L, H, &bytes) != H3A_OK) return -1;
-  ok();
-  return h3attn::attention_workspace_bytes(L, H);
-}
-
 int h3attn_forward(const void* q, const void* k, const void* v, void* out, int64_t L, int32_t H,
-                   float scale, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !out || !workspace) return fail(H3A_EINVAL, "null pointer argument%s");
+                   float scale, hipStream_t stream) {
+  if (!q || !k || !v || !out) return fail(H3A_EINVAL, "null pointer argument%s");
   uint64_t bytes = 0;
   if (int s = check_shape(L, H, &bytes)) return s;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(workspace, 16))
-    return fail(H3A_EINVAL, "q, k, v, out and workspace must be 16-byte aligned%s");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(H3A_EINVAL, "q, k, v and out must be 16-byte aligned%s");
   if (!(isfinite(scale) && scale > 0.0f)) return fail(H3A_EINVAL, "scale must be finite and > 0%s");
-  const int64_t ws_need = h3attn::attention_workspace_bytes(L, H);
-  if (workspace_bytes < ws_need)
-    return fail(H3A_EINVAL, "workspace_bytes is below h3attn_forward_workspace_bytes(L, H)%s");
   if (overlap(out, bytes, q, bytes) || overlap(out, bytes, k, bytes) || overlap(out, bytes, v, bytes))
     return fail(H3A_EINVAL, "out overlaps q, k or v%s");
-  if (overlap(workspace, (uint64_t)ws_need, q, bytes) || overlap(workspace, (uint64_t)ws_need, k, bytes) ||
-      overlap(workspace, (uint64_t)ws_need, v, bytes) || overlap(workspace, (uint64_t)ws_need, out, bytes))
-    return fail(H3A_EINVAL, "workspace overlaps q, k, v or out%s");
-  if (h3attn::attention_grid_blocks(L, H) * h3attn::attention_block_threads() >= kMaxThreadsPerGrid ||
-      h3attn::transpose_grid_blocks(L, H) * h3attn::transpose_block_threads() >= kMaxThreadsPerGrid)
+  if (h3attn::attention_grid_blocks(L, H) * h3attn::attention_block_threads() >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "attention grid too large for (L, H)%s");
   const hipError_t e = h3attn::launch_attention_forward(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-      static_cast<uint16_t*>(out), static_cast<uint16_t*>(workspace), L, H, scale, stream);
+      static_cast<uint16_t*>(out), L, H, scale, stream);
   if (e != hipSuccess) return fail(H3A_EHIP, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
 }

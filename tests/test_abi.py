@@ -34,7 +34,7 @@ def test_header_declares_the_expected_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.h3attn_abi_version() == 2
+    assert lib.h3attn_abi_version() == 1
 
 
 def test_strerror_strings(lib):
@@ -51,26 +51,14 @@ C = 0x7F2000000000
 O = 0x7F3000000000
 G = 0x7F4000000000
 P = 0x7F5000000000
-W = 0x7F6000000000
 
 
 def prologue(lib, q=A, k=B, gq=G, gk=G + 512, pos=P, L=160, H=4):
     return lib.h3attn_qk_prologue(q, k, gq, gk, pos, L, H, None)
 
 
-def forward(lib, q=A, k=B, v=C, out=O, L=160, H=4, scale=0.08838834764831845, ws=W, ws_bytes=None):
-    if ws_bytes is None:
-        ws_bytes = max(lib.h3attn_forward_workspace_bytes(L, H), 0)
-    return lib.h3attn_forward(q, k, v, out, L, H, scale, ws, ws_bytes, None)
-
-
-@pytest.mark.parametrize("L,H,want", [
-    (160, 4, 4 * 128 * 192 * 2), (64, 1, 128 * 64 * 2), (65, 1, 128 * 128 * 2), (1, 56, 56 * 128 * 64 * 2),
-    (16500, 56, 56 * 128 * 16512 * 2), (0, 4, -1), (160, 0, -1), (1 << 31, 1, -1),
-])
-def test_forward_workspace_bytes(lib, L, H, want):
-    # H * 128 * (L rounded up to 64) bf16 values: the transposed copy of v.
-    assert lib.h3attn_forward_workspace_bytes(L, H) == want
+def forward(lib, q=A, k=B, v=C, out=O, L=160, H=4, scale=0.08838834764831845):
+    return lib.h3attn_forward(q, k, v, out, L, H, scale, None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -96,10 +84,7 @@ def test_prologue_rejects(lib, kw, code, msg):
     (dict(scale=float("inf")), 1, "scale"),
     (dict(out=A), 1, "overlap"), (dict(out=B + 1024), 1, "overlap"), (dict(out=C - 1024), 1, "overlap"),
     (dict(L=1 << 31), 2, "2^31"),
-    (dict(L=(1 << 31) - 1, H=56, q=1 << 46, k=2 << 46, v=3 << 46, out=4 << 46, ws=5 << 46), 2, "grid"),
-    (dict(ws=None), 1, "null"), (dict(ws=W + 8), 1, "aligned"),
-    (dict(ws_bytes=4 * 128 * 192 * 2 - 16), 1, "workspace_bytes"), (dict(ws_bytes=-1), 1, "workspace_bytes"),
-    (dict(ws=A + 1024), 1, "workspace overlaps"), (dict(ws=O - 4 * 128 * 192 * 2 + 16), 1, "workspace overlaps"),
+    (dict(L=(1 << 31) - 1, H=56, q=1 << 46, k=2 << 46, v=3 << 46, out=4 << 46), 2, "grid"),
 ])
 def test_forward_rejects(lib, kw, code, msg):
     assert forward(lib, **kw) == code
