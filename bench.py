@@ -2,6 +2,12 @@
 over the long single-GPU packed document: L = 16500 tokens (256 text +
 36x15x27 video + 1664 audio), H = 56 heads of 128.
 
+The timed step is the scale-folded form of the path: h3attn_qk_prologue_scaled
+(Q's output carries scale * log2(e), applied before its one bf16 rounding) then
+h3attn_forward_log2 (base-2 softmax).  It computes the same attention with the
+same roundings as h3attn_qk_prologue + h3attn_forward, which are timed beside
+it and reported under "plain_path".
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
                     [--no-cpu-baseline] [--copy-probe]
 
@@ -109,7 +115,8 @@ def main() -> int:
 
     import numpy as np
     import torch
-    from packed_full_attention_amd import h3attn_forward, h3attn_qk_prologue, load_library
+    from packed_full_attention_amd import (h3attn_forward, h3attn_forward_log2, h3attn_qk_prologue,
+                                           h3attn_qk_prologue_scaled, load_library)
     from packed_full_attention_amd import workloads as wl
 
     load_library()
@@ -123,6 +130,7 @@ def main() -> int:
     pos = torch.from_numpy(inp.pos).to(dev)
     out = torch.empty_like(q)
     scale = 1.0 / math.sqrt(128.0)
+    q_scale = float(np.float32(scale * math.log2(math.e)))
 
     if args.copy_probe:
         a = torch.ones(256 << 20, dtype=torch.uint8, device=dev).view(torch.int32)
@@ -132,33 +140,40 @@ def main() -> int:
         print(json.dumps({"copy_probe_bytes_read": 256 << 20, "copy_probe_bytes_written": 256 << 20}),
               file=sys.stderr)
 
-    def step():
-        h3attn_qk_prologue(q, k, gq, gk, pos)
-        h3attn_forward(q, k, v, out, scale=scale)
+    def timed(prologue, forward, K):
+        """Average ms per step, per prologue launch and per forward launch over K steps."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for i in range(K):
+            ev[i][0].record(stream)
+            prologue()
+            ev[i][1].record(stream)
+            forward()
+            ev[i][2].record(stream)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        return (start.elapsed_time(stop) / K, sum(e[0].elapsed_time(e[1]) for e in ev) / K,
+                sum(e[1].elapsed_time(e[2]) for e in ev) / K, wall)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    pro_s = lambda: h3attn_qk_prologue_scaled(q, k, gq, gk, pos, q_scale)
+    fwd_s = lambda: h3attn_forward_log2(q, k, v, out)
+    pro_p = lambda: h3attn_qk_prologue(q, k, gq, gk, pos)
+    fwd_p = lambda: h3attn_forward(q, k, v, out, scale=scale)
 
     K = args.steps
-    stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(K):
-        ev[i][0].record(stream)
-        h3attn_qk_prologue(q, k, gq, gk, pos)
-        ev[i][1].record(stream)
-        h3attn_forward(q, k, v, out, scale=scale)
-        ev[i][2].record(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    ms_step = start.elapsed_time(stop) / K
-    t_pro = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    t_att = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    for _ in range(args.warmup):
+        pro_p()
+        fwd_p()
+    plain_ms, plain_pro, plain_att, _ = timed(pro_p, fwd_p, K)
+    for _ in range(args.warmup):
+        pro_s()
+        fwd_s()
+    ms_step, t_pro, t_att, wall_ms = timed(pro_s, fwd_s, K)
     if not bool(torch.isfinite(out.float()).all()):
         print("bench.py: non-finite attention output", file=sys.stderr)
         return 1
@@ -183,13 +198,17 @@ def main() -> int:
         "config": {"workload": f"packed full attention {w.describe()}, bf16 q/k/v ~N(0,1), "
                                f"gammas 1+0.1N(0,1), seed {1000 + w.index}",
                    "L": L, "H": H, "head_dim": 128, "scale": "1/sqrt(128)"},
-        "roofline": {"bound": "mfma", "kernel": "attention_fwd_kernel", "achieved": round(att_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "attention_fwd_kernel<log2>", "achieved": round(att_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(t_att, 4)},
         "prologue": {"bound": "hbm", "kernel": "qk_prologue_kernel", "achieved": round(pro_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pro_gbs / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes": prologue_bytes(L, H), "avg_launch_us": round(t_pro * 1e3, 2)},
+        "plain_path": {"entry_points": "h3attn_qk_prologue + h3attn_forward", "ms_per_step": round(plain_ms, 4),
+                       "attention_ms": round(plain_att, 4),
+                       "attention_tflops": round(flops / (plain_att * 1e-3) / 1e12, 2),
+                       "prologue_us": round(plain_pro * 1e3, 2)},
         "wall_ms_timed_region": round(wall_ms, 2),
     }
     if not args.no_cpu_baseline:

@@ -44,13 +44,13 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 1
+#define H3ATTN_ABI_VERSION 2
 #define H3ATTN_HEAD_DIM 128
 
 /* Status codes. */
 #define H3A_OK 0            /* success (work enqueued)                               */
 #define H3A_EINVAL 1        /* null pointer, L <= 0, H <= 0, misalignment, overlap,   */
-                            /* or a non-finite / non-positive scale                   */
+                            /* or a non-finite / non-positive scale or q_scale        */
 #define H3A_EUNSUPPORTED 2  /* geometry outside the supported range (L >= 2^31,       */
                             /* grid or size overflow)                                 */
 #define H3A_EHIP 3          /* the HIP launch reported an error                       */
@@ -97,6 +97,32 @@ int h3attn_qk_prologue(void* q, void* k, const float* gamma_q, const float* gamm
  */
 int h3attn_forward(const void* q, const void* k, const void* v, void* out, int64_t L,
                    int32_t H, float scale, hipStream_t stream);
+
+/*
+ * The same path with the softmax scale folded into q.  Together,
+ *   h3attn_qk_prologue_scaled(q, k, gamma_q, gamma_k, pos_thw, L, H, scale * log2(e), s)
+ *   h3attn_forward_log2(q, k, v, out, L, H, s)
+ * compute what h3attn_qk_prologue + h3attn_forward(..., scale, s) compute, with
+ * the same single bf16 rounding of q (of the scaled values instead of the
+ * unscaled ones); the attention kernel then evaluates each exponential straight
+ * from the matrix-core score, without a scaling instruction per score.
+ *
+ * h3attn_qk_prologue_scaled: as h3attn_qk_prologue, except that the Q output
+ *   is multiplied by q_scale (finite, > 0; applied in fp32 before the rounding
+ *   to bf16).  q_scale = 1 gives h3attn_qk_prologue's output bit for bit.
+ *
+ * h3attn_forward_log2: base-2 softmax attention, per head h,
+ *   out[i,h,:] = sum_j 2^<q[i,h,:], k[j,h,:]> v[j,h,:] / sum_j 2^<q[i,h,:], k[j,h,:]>
+ *   i.e. h3attn_forward with scale = ln 2 (and so, with q from
+ *   h3attn_qk_prologue_scaled at q_scale = scale * log2(e), the scale-`scale`
+ *   attention of the unscaled q).  Arguments, layouts, ownership and errors as
+ *   for h3attn_forward.
+ */
+int h3attn_qk_prologue_scaled(void* q, void* k, const float* gamma_q, const float* gamma_k,
+                              const int32_t* pos_thw, int64_t L, int32_t H, float q_scale,
+                              hipStream_t stream);
+int h3attn_forward_log2(const void* q, const void* k, const void* v, void* out, int64_t L,
+                        int32_t H, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* h3attn_strerror(int status);

@@ -17,8 +17,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libh3attn.so")
 HEAD_DIM = 128
 H3A_OK, H3A_EINVAL, H3A_EUNSUPPORTED, H3A_EHIP = 0, 1, 2, 3
-EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward", "h3attn_strerror",
-                    "h3attn_last_error", "h3attn_abi_version")
+EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward", "h3attn_qk_prologue_scaled",
+                    "h3attn_forward_log2", "h3attn_strerror", "h3attn_last_error", "h3attn_abi_version")
 
 _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
@@ -45,6 +45,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.h3attn_qk_prologue.restype = ctypes.c_int
         lib.h3attn_forward.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, vp]
         lib.h3attn_forward.restype = ctypes.c_int
+        lib.h3attn_qk_prologue_scaled.argtypes = [vp, vp, vp, vp, vp, i64, i32, ctypes.c_float, vp]
+        lib.h3attn_qk_prologue_scaled.restype = ctypes.c_int
+        lib.h3attn_forward_log2.argtypes = [vp, vp, vp, vp, i64, i32, vp]
+        lib.h3attn_forward_log2.restype = ctypes.c_int
         lib.h3attn_strerror.argtypes = [ctypes.c_int]
         lib.h3attn_strerror.restype = ctypes.c_char_p
         lib.h3attn_last_error.argtypes = []
@@ -85,8 +89,7 @@ def _lh(q):
     return int(q.shape[0]), int(q.shape[1])
 
 
-def h3attn_qk_prologue(q, k, gamma_q, gamma_k, pos_thw) -> None:
-    """In-place Q/K RMSNorm + MM-RoPE on bf16 [L, H, 128] q and k (see include/h3attn.h)."""
+def _prologue(fn: str, q, k, gamma_q, gamma_k, pos_thw, q_scale) -> None:
     import torch
     L, H = _lh(q)
     dev = q.device
@@ -98,13 +101,25 @@ def h3attn_qk_prologue(q, k, gamma_q, gamma_k, pos_thw) -> None:
     lib = load_library()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        st = lib.h3attn_qk_prologue(q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(),
-                                    pos_thw.data_ptr(), L, H, stream)
-    _raise_on(lib, "h3attn_qk_prologue", st)
+        args = (q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(), pos_thw.data_ptr(), L, H)
+        if q_scale is None:
+            st = lib.h3attn_qk_prologue(*args, stream)
+        else:
+            st = lib.h3attn_qk_prologue_scaled(*args, float(q_scale), stream)
+    _raise_on(lib, fn, st)
 
 
-def h3attn_forward(q, k, v, out=None, scale: Optional[float] = None):
-    """Full bidirectional attention on bf16 [L, H, 128]; returns out (see include/h3attn.h)."""
+def h3attn_qk_prologue(q, k, gamma_q, gamma_k, pos_thw) -> None:
+    """In-place Q/K RMSNorm + MM-RoPE on bf16 [L, H, 128] q and k (see include/h3attn.h)."""
+    _prologue("h3attn_qk_prologue", q, k, gamma_q, gamma_k, pos_thw, None)
+
+
+def h3attn_qk_prologue_scaled(q, k, gamma_q, gamma_k, pos_thw, q_scale: float) -> None:
+    """h3attn_qk_prologue with Q's output multiplied by q_scale before its bf16 rounding."""
+    _prologue("h3attn_qk_prologue_scaled", q, k, gamma_q, gamma_k, pos_thw, q_scale)
+
+
+def _forward(fn: str, q, k, v, out, scale):
     import torch
     L, H = _lh(q)
     dev = q.device
@@ -114,15 +129,26 @@ def h3attn_forward(q, k, v, out=None, scale: Optional[float] = None):
     if out is None:
         out = torch.empty_like(q)
     _check_tensor("out", out, torch.bfloat16, (L, H, HEAD_DIM), dev)
-    if scale is None:
-        scale = 1.0 / math.sqrt(HEAD_DIM)
     lib = load_library()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        st = lib.h3attn_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), L, H,
-                                float(scale), stream)
-    _raise_on(lib, "h3attn_forward", st)
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), L, H)
+        if scale is None:
+            st = lib.h3attn_forward_log2(*args, stream)
+        else:
+            st = lib.h3attn_forward(*args, float(scale), stream)
+    _raise_on(lib, fn, st)
     return out
+
+
+def h3attn_forward(q, k, v, out=None, scale: Optional[float] = None):
+    """Full bidirectional attention on bf16 [L, H, 128]; returns out (see include/h3attn.h)."""
+    return _forward("h3attn_forward", q, k, v, out, 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale)
+
+
+def h3attn_forward_log2(q, k, v, out=None):
+    """Base-2 softmax attention (q carries the softmax scale times log2(e)); returns out."""
+    return _forward("h3attn_forward_log2", q, k, v, out, None)
 
 
 def abi_version() -> int:

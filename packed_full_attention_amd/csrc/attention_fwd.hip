@@ -5,6 +5,16 @@
 // and unmasked over one packed document"; section 5 item h3_full_attention):
 //   out[i,h,:] = sum_j softmax_j(scale * <q[i,h,:], k[j,h,:]>) v[j,h,:]
 //
+// Two variants of one kernel.  The plain one computes exactly that, with the
+// scale applied in fp32 to each score.  The log2 one expects q to carry
+// scale * log2(e) already (the Q/K prologue applies it in fp32 before q's
+// single rounding to bf16, so q is rounded once either way) and computes
+//   out[i,h,:] = sum_j 2^<q[i,h,:], k[j,h,:]> v[j,h,:] / sum_j 2^<q[i,h,:], k[j,h,:]>
+// which is the same softmax: its scores come out of the matrix cores in the
+// exponent's units, and the offset is subtracted there too (the score MFMA
+// chain starts from -m instead of 0), so no vector instruction stands between
+// a score and its exponential.
+//
 // Numerical contract (same RFC, section 4): fp32 accumulation on the matrix
 // cores, one fixed key order (tile 0, 1, 2, ...), no split over keys, no
 // atomics; every output row is produced by exactly one wave, so the result
@@ -197,7 +207,8 @@ __device__ __forceinline__ void cold_path() { asm volatile("" ::: "memory"); }
 struct State {
   bf16x8_t q[8];   // Q^T operand: q[ks] = Q[row][16 ks + 8 g .. +7]
   f32x16_t o[4];   // O^T accumulators, d-blocks of 32
-  float m;         // exponent offset (raw score units)
+  f32x16_t minit;  // log2 variant: -m in every slot, the score chain's start
+  float m;         // exponent offset (raw score units; log2 variant: log2 units)
   float l;         // this lane-half's partial sum of P
 };
 
@@ -249,12 +260,19 @@ __device__ __forceinline__ void pv(State& st, const bf16x8_t (&p)[4], const lds_
 // Weights.  Score n (0..31) of a lane is accumulator slot n % 16 of block
 // n / 16; its weight P = 2^(c s - mc) (mc = c m) is rounded to bf16 and paired
 // with its neighbour: pair i = n / 2 is dword i % 4 of the P^T operand p[i / 4]
-// (low half: the even score).  The lane sum adds exactly these bf16 values,
-// read back from the packed pair -- the high half as a float is
-// (bits & 0xffff0000), the low half (bits << 16) -- with plain fp32 adds, which
-// the SIMD issues alongside the matrix instructions (a v_dot2_f32_bf16 against
-// (1, 1) would add the same values but stalls the matrix pipe).
+// (low half: the even score).  The lane sum adds exactly these bf16 values.
+// In the pipelined loop it runs on the matrix cores: v_mfma_f32_4x4x4bf16_1k
+// with A = ones returns in every lane the fp32 sum of that lane's own four B
+// values, so eight of them (two packed pairs each) add up a tile; the vector
+// units, which the softmax already loads beyond what the matrix instructions
+// hide, are spared the 63 instructions of a VALU sum (v_dot2_f32_bf16 against
+// (1, 1) is no better: it stalls the matrix pipe for longer than a 4x4x4 MFMA).
+// The unscheduled form below, for the first tile and the rare path, reads the
+// pair back instead -- the high half as a float is (bits & 0xffff0000), the low
+// half (bits << 16) -- and adds in fp32.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
@@ -305,6 +323,33 @@ __device__ __forceinline__ float rebase(const f32x16_t (&s_in)[2], State& st, fl
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.o[i] *= alpha;
   return weights(s, c, m_new * c, p);
+}
+
+// Rare path of the log2 variant, where the accumulators hold score - m: move
+// m up to the tile's row maximum when that exceeds it, scale O and l, shift the
+// next tile's scores (computed against the old m) and the chain start, and
+// recompute the tile's weights.
+__device__ __forceinline__ float rebase_log2(const f32x16_t (&s_in)[2], f32x16_t (&s_next)[2], State& st,
+                                             bf16x8_t (&p)[4]) {
+  f32x16_t s[2] = {s_in[0], s_in[1]};
+  asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+  float m0 = fmaxf(s[0][0], s[0][1]);
+  float m1 = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+  for (int e = 2; e < 16; e += 2) {
+    m0 = fmaxf(fmaxf(m0, s[0][e]), s[0][e + 1]);
+    m1 = fmaxf(fmaxf(m1, s[1][e]), s[1][e + 1]);
+  }
+  const float delta = fmaxf(pair_max(fmaxf(m0, m1)), 0.f);  // m_new - m_old, same in both halves
+  const float alpha = __builtin_amdgcn_exp2f(-delta);
+  st.m += delta;
+  st.l *= alpha;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.o[i] *= alpha;
+  s_next[0] -= delta;
+  s_next[1] -= delta;
+  st.minit -= delta;
+  return weights(s, 1.f, delta, p);
 }
 
 // Scores of keys at or past L (only in the last, partial tile) become -inf.
@@ -364,12 +409,11 @@ __device__ __forceinline__ bf16x8_t slot_operand(int k, const lds_char* lds, con
 // slot, with scheduling barriers in between: the operand read of slot k + 2,
 // the MFMA of slot k, then a share of the weights, each step one slot after
 // the one it depends on -- the FMA of score k, the exponential of score k - 1,
-// on odd slots the bf16 pack of pair (k - 3) / 2, and the row-sum terms of the
-// pairs before it.  A slot then holds one transcendental and three or four
-// plain VALU instructions, which the SIMD executes under the 32-cycle matrix
-// instruction; four more slots without a matrix instruction finish the last
-// pairs.
-template <bool kPV>
+// on odd slots the bf16 pack of pair (k - 3) / 2, and every fourth slot the
+// 4x4x4 MFMA that adds two packed pairs to the row sum.  A slot then holds one
+// transcendental and one or two plain VALU instructions next to its 32-cycle
+// matrix instruction; four more slots without one finish the last pairs.
+template <bool kPV, bool kLog2>
 __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, const f32x16_t (&s_cur)[2],
                                           f32x16_t (&s_next)[2], const bf16x8_t (&p_prev)[4],
                                           bf16x8_t (&p_cur)[4], int t) {
@@ -380,12 +424,13 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
 
   const float c = x.c, mc = st.m * c;
   float psum;
-  s_next[0] = f32x16_t{};
-  s_next[1] = f32x16_t{};
+  s_next[0] = kLog2 ? st.minit : f32x16_t{};
+  s_next[1] = kLog2 ? st.minit : f32x16_t{};
   if (kPV) {
     float xs[32];
     uint32_t w[16];
-    float hi, lo;
+    const i16x4_t ones4 = {16256, 16256, 16256, 16256};  // bf16 1.0
+    f32x4_t sum4 = {0.f, 0.f, 0.f, 0.f};
     bf16x8_t op[32];
     op[0] = slot_operand(0, x.lds, b);
     op[1] = slot_operand(1, x.lds, b);
@@ -407,7 +452,7 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
         } else {
           st.o[i & 3] = mfma32(op[k], p_prev[i >> 2], st.o[i & 3]);
         }
-        xs[k] = fmaf(s_cur[k >> 4][k & 15], c, -mc);
+        xs[k] = kLog2 ? s_cur[k >> 4][k & 15] : fmaf(s_cur[k >> 4][k & 15], c, -mc);
       }
       if (k >= 1 && k <= 32) xs[k - 1] = __builtin_amdgcn_exp2f(xs[k - 1]);
       if ((k & 1) == 1 && k >= 3) {
@@ -417,14 +462,16 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
         // conversion of one of its halves.
         asm volatile("" : "+v"(w[i]));
       }
-      if (k == 4) hi = hi_bf16(w[0]);
-      if ((k & 1) == 0 && k >= 6) hi += hi_bf16(w[(k - 4) >> 1]);
-      if (k == 5) lo = lo_bf16(w[0]);
-      if ((k & 1) == 1 && k >= 7) lo += lo_bf16(w[(k - 5) >> 1]);
+      if (k >= 6 && ((k - 6) & 3) == 0 && ((k - 6) >> 2) < 8) {
+        // Pairs 2i and 2i+1 (packed on slots 4i+3 and 4i+5) into the row sum.
+        const int i = (k - 6) >> 2;
+        const i16x4_t b4 = __builtin_bit_cast(i16x4_t, u32x2_t{w[2 * i], w[2 * i + 1]});
+        sum4 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ones4, b4, sum4, 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     store_pairs(w, p_cur);
-    psum = hi + lo;
+    psum = sum4[0];
   } else {
     dma_all(kd, x.dma);
     dma_all(vd, x.dma);
@@ -432,11 +479,11 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s_next[kb] = mfma32(k_operand(kb, ks, x.lds, b), st.q[ks], s_next[kb]);
-    psum = weights(s_cur, c, mc, p_cur);
+    psum = kLog2 ? weights(s_cur, 1.f, 0.f, p_cur) : weights(s_cur, c, mc, p_cur);
   }
   if (__builtin_amdgcn_ballot_w64(!(psum <= kSumBound)) != 0) {
     cold_path();
-    psum = rebase(s_cur, st, c, p_cur);
+    psum = kLog2 ? rebase_log2(s_cur, s_next, st, p_cur) : rebase(s_cur, st, c, p_cur);
   }
   st.l += psum;
   if (t + 1 >= x.n_full) {
@@ -447,6 +494,7 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
   __syncthreads();  // K(t+2), V(t) landed; every wave is done with K(t+1), V(t-1)
 }
 
+template <bool kLog2>
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, int L, int H, float scale_log2e, int n_qtiles) {
@@ -525,22 +573,38 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
       for (int kb = 0; kb < 2; ++kb) s0[kb] = mfma32(k_operand(kb, ks, x.lds, b0), st.q[ks], s0[kb]);
   }
   if (x.n_full == 0) mask_tail(s0, 0, L, x.g);
+  if (kLog2) {
+    // The offset starts at the first tile's row maximum, so no tile needs
+    // the -FLT_MAX start (which would swamp the scores held relative to m).
+    float m0 = fmaxf(s0[0][0], s0[0][1]);
+    float m1 = fmaxf(s0[1][0], s0[1][1]);
+#pragma unroll
+    for (int e = 2; e < 16; e += 2) {
+      m0 = fmaxf(fmaxf(m0, s0[0][e]), s0[0][e + 1]);
+      m1 = fmaxf(fmaxf(m1, s0[1][e]), s0[1][e + 1]);
+    }
+    st.m = pair_max(fmaxf(m0, m1));
+    s0[0] -= st.m;
+    s0[1] -= st.m;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.minit[i] = -st.m;
+  }
   // The first iteration refills K(0)'s slot with K(3): every wave must be done
   // reading K(0) first.  (Later refills are ordered by the previous
   // iteration's barrier.)
   __syncthreads();
 
   // S(t) and P(t) live in s/p[t % 2]; odd/even pairs keep that choice static.
-  iteration<false>(x, st, a, s0, s1, p1, p0, 0);
+  iteration<false, kLog2>(x, st, a, s0, s1, p1, p0, 0);
   int t = 1;
   for (; t + 1 < x.n_tiles; t += 2) {
-    iteration<true>(x, st, a, s1, s0, p0, p1, t);
-    iteration<true>(x, st, a, s0, s1, p1, p0, t + 1);
+    iteration<true, kLog2>(x, st, a, s1, s0, p0, p1, t);
+    iteration<true, kLog2>(x, st, a, s0, s1, p1, p0, t + 1);
   }
   // P(n-1) V(n-1); V(n-1) landed before the last iteration's barrier.
   const Addr b_last = at_buffers(a, 0, kVRing + ring(x.n_tiles - 1));
   if (t < x.n_tiles) {
-    iteration<true>(x, st, a, s1, s0, p0, p1, t);
+    iteration<true, kLog2>(x, st, a, s1, s0, p0, p1, t);
     pv(st, p1, x.lds, b_last);
   } else {
     pv(st, p0, x.lds, b_last);
@@ -569,11 +633,16 @@ int64_t attention_grid_blocks(int64_t L, int32_t H) { return ((L + kBM - 1) / kB
 int attention_block_threads() { return kThreads; }
 
 hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                    uint16_t* out, int64_t L, int32_t H, float scale, hipStream_t stream) {
+                                    uint16_t* out, int64_t L, int32_t H, float scale, bool log2,
+                                    hipStream_t stream) {
   const int n_qtiles = (int)((L + kBM - 1) / kBM);
   const dim3 grid((unsigned)attention_grid_blocks(L, H));
-  hipLaunchKernelGGL(attention_fwd_kernel, grid, dim3(kThreads), 0, stream, q, k, v, out, (int)L, (int)H,
-                     scale * kLog2e, n_qtiles);
+  if (log2)
+    hipLaunchKernelGGL(attention_fwd_kernel<true>, grid, dim3(kThreads), 0, stream, q, k, v, out, (int)L,
+                       (int)H, 1.0f, n_qtiles);
+  else
+    hipLaunchKernelGGL(attention_fwd_kernel<false>, grid, dim3(kThreads), 0, stream, q, k, v, out, (int)L,
+                       (int)H, scale * kLog2e, n_qtiles);
   return hipGetLastError();
 }
 

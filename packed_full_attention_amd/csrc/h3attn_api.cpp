@@ -65,8 +65,10 @@ const char* h3attn_strerror(int status) {
 
 const char* h3attn_last_error(void) { return g_last_error; }
 
-int h3attn_qk_prologue(void* q, void* k, const float* gamma_q, const float* gamma_k,
-                       const int32_t* pos_thw, int64_t L, int32_t H, hipStream_t stream) {
+namespace {
+
+int prologue(void* q, void* k, const float* gamma_q, const float* gamma_k, const int32_t* pos_thw, int64_t L,
+             int32_t H, float q_scale, hipStream_t stream) {
   if (!q || !k || !gamma_q || !gamma_k || !pos_thw)
     return fail(H3A_EINVAL, "null pointer argument%s");
   uint64_t bytes = 0;
@@ -74,17 +76,18 @@ int h3attn_qk_prologue(void* q, void* k, const float* gamma_q, const float* gamm
   if (!aligned(q, 16) || !aligned(k, 16)) return fail(H3A_EINVAL, "q and k must be 16-byte aligned%s");
   if (!aligned(gamma_q, 4) || !aligned(gamma_k, 4) || !aligned(pos_thw, 4))
     return fail(H3A_EINVAL, "gamma_q, gamma_k and pos_thw must be 4-byte aligned%s");
+  if (!(isfinite(q_scale) && q_scale > 0.0f)) return fail(H3A_EINVAL, "q_scale must be finite and > 0%s");
   if (overlap(q, bytes, k, bytes)) return fail(H3A_EINVAL, "q and k overlap%s");
   if (h3attn::prologue_grid_blocks(L) * 256 >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "prologue grid too large for L%s");
   const hipError_t e = h3attn::launch_qk_prologue(static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
-                                                  gamma_q, gamma_k, pos_thw, L, H, stream);
+                                                  gamma_q, gamma_k, pos_thw, L, H, q_scale, stream);
   if (e != hipSuccess) return fail(H3A_EHIP, "prologue launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
-int h3attn_forward(const void* q, const void* k, const void* v, void* out, int64_t L, int32_t H,
-                   float scale, hipStream_t stream) {
+int forward(const void* q, const void* k, const void* v, void* out, int64_t L, int32_t H, float scale,
+            bool log2, hipStream_t stream) {
   if (!q || !k || !v || !out) return fail(H3A_EINVAL, "null pointer argument%s");
   uint64_t bytes = 0;
   if (int s = check_shape(L, H, &bytes)) return s;
@@ -97,9 +100,31 @@ int h3attn_forward(const void* q, const void* k, const void* v, void* out, int64
     return fail(H3A_EUNSUPPORTED, "attention grid too large for (L, H)%s");
   const hipError_t e = h3attn::launch_attention_forward(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-      static_cast<uint16_t*>(out), L, H, scale, stream);
+      static_cast<uint16_t*>(out), L, H, scale, log2, stream);
   if (e != hipSuccess) return fail(H3A_EHIP, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+int h3attn_qk_prologue(void* q, void* k, const float* gamma_q, const float* gamma_k,
+                       const int32_t* pos_thw, int64_t L, int32_t H, hipStream_t stream) {
+  return prologue(q, k, gamma_q, gamma_k, pos_thw, L, H, 1.0f, stream);
+}
+
+int h3attn_qk_prologue_scaled(void* q, void* k, const float* gamma_q, const float* gamma_k,
+                              const int32_t* pos_thw, int64_t L, int32_t H, float q_scale, hipStream_t stream) {
+  return prologue(q, k, gamma_q, gamma_k, pos_thw, L, H, q_scale, stream);
+}
+
+int h3attn_forward(const void* q, const void* k, const void* v, void* out, int64_t L, int32_t H,
+                   float scale, hipStream_t stream) {
+  return forward(q, k, v, out, L, H, scale, false, stream);
+}
+
+int h3attn_forward_log2(const void* q, const void* k, const void* v, void* out, int64_t L, int32_t H,
+                        hipStream_t stream) {
+  return forward(q, k, v, out, L, H, 1.0f, true, stream);
 }
 
 }  // extern "C"

@@ -7,14 +7,17 @@
 
 namespace h3attn {
 
-// Enqueue the fused Q/K RMSNorm + MM-RoPE kernel (in place on q and k).
+// Enqueue the fused Q/K RMSNorm + MM-RoPE kernel (in place on q and k); Q's
+// output is multiplied by q_scale before its rounding to bf16.
 hipError_t launch_qk_prologue(uint16_t* q, uint16_t* k, const float* gamma_q,
                               const float* gamma_k, const int32_t* pos, int64_t L, int32_t H,
-                              hipStream_t stream);
+                              float q_scale, hipStream_t stream);
 
-// Enqueue the flash-attention forward kernel.
+// Enqueue the flash-attention forward kernel.  log2 = false: weights
+// exp(scale <q,k>); log2 = true: weights 2^<q,k> (q already carries the
+// softmax scale times log2(e)), scale ignored.
 hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                    uint16_t* out, int64_t L, int32_t H, float scale,
+                                    uint16_t* out, int64_t L, int32_t H, float scale, bool log2,
                                     hipStream_t stream);
 
 // Grid size (workgroups) and workgroup size (threads) of the forward launch

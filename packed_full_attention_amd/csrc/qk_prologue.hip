@@ -10,6 +10,9 @@
 //   for c < 48:  out_c = y_c cos phi_c - y_{c+48} sin phi_c
 //                out_{c+48} = y_{c+48} cos phi_c + y_c sin phi_c
 //   out_c = y_c for 96 <= c < 128;   one RNE rounding to bf16 at the end.
+// Q's output may carry a scale factor q_scale (applied in fp32, folded into
+// gamma_q, before that single rounding); q_scale = 1 leaves every bit as
+// above.
 //
 // Memory-bound by construction: every Q and K head-row is read once (256 B)
 // and written once, in place.  Mapping: one wave per token.  A quarter-wave
@@ -45,7 +48,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
     uint16_t* __restrict__ q, uint16_t* __restrict__ k, const float* __restrict__ gamma_q,
-    const float* __restrict__ gamma_k, const int32_t* __restrict__ pos, int64_t L, int32_t H) {
+    const float* __restrict__ gamma_k, const int32_t* __restrict__ pos, int64_t L, int32_t H,
+    float q_scale) {
   const int lane = threadIdx.x & 63;
   const int64_t token = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (token >= L) return;  // whole wave exits together
@@ -60,8 +64,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
   float gqa[4], gqb[4], gka[4], gkb[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    gqa[e] = gamma_q[ch_a + e];
-    gqb[e] = gamma_q[ch_b + e];
+    gqa[e] = gamma_q[ch_a + e] * q_scale;
+    gqb[e] = gamma_q[ch_b + e] * q_scale;
     gka[e] = gamma_k[ch_a + e];
     gkb[e] = gamma_k[ch_b + e];
   }
@@ -132,10 +136,10 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
 int64_t prologue_grid_blocks(int64_t L) { return (L + kWavesPerBlock - 1) / kWavesPerBlock; }
 
 hipError_t launch_qk_prologue(uint16_t* q, uint16_t* k, const float* gamma_q, const float* gamma_k,
-                              const int32_t* pos, int64_t L, int32_t H, hipStream_t stream) {
+                              const int32_t* pos, int64_t L, int32_t H, float q_scale, hipStream_t stream) {
   const dim3 grid((unsigned)prologue_grid_blocks(L));
   hipLaunchKernelGGL(qk_prologue_kernel, grid, dim3(kWavesPerBlock * 64), 0, stream, q, k, gamma_q,
-                     gamma_k, pos, L, H);
+                     gamma_k, pos, L, H, q_scale);
   return hipGetLastError();
 }
 

@@ -28,3 +28,17 @@ def dev_inputs(inp: wl.Inputs):
 def head_f64(bits: np.ndarray):
     """Accessor h -> float64 [L, 128] slice of a bf16 [L, H, 128] array."""
     return lambda h: wl.bf16_bits_to_f32(np.ascontiguousarray(bits[:, h, :])).astype(np.float64)
+
+
+def sample_rows(w: wl.Workload, n: int, seed: int) -> np.ndarray:
+    """Rows checked one by one on the long workloads: modality boundaries, the
+    last two 64-key tiles, and n random rows."""
+    L = w.seq_len
+    special = [0, 1, w.n_text - 1, w.n_text, w.n_text + w.n_video - 1, w.n_text + w.n_video,
+               L - 129, L - 128, L - 65, L - 64, L - 2, L - 1]
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([special, rng.choice(L, n, replace=False)])).astype(np.int64)
+
+
+def sample_heads(w: wl.Workload) -> np.ndarray:
+    return np.unique([0, w.heads // 3, (2 * w.heads) // 3, w.heads - 1]).astype(np.int64)

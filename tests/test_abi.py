@@ -34,7 +34,7 @@ def test_header_declares_the_expected_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.h3attn_abi_version() == 1
+    assert lib.h3attn_abi_version() == 2
 
 
 def test_strerror_strings(lib):
@@ -89,6 +89,17 @@ def test_prologue_rejects(lib, kw, code, msg):
 def test_forward_rejects(lib, kw, code, msg):
     assert forward(lib, **kw) == code
     assert msg in lib.h3attn_last_error().decode()
+
+
+def test_scaled_entry_points_reject(lib):
+    f = lambda **kw: lib.h3attn_qk_prologue_scaled(kw.get("q", A), B, G, G + 512, P, kw.get("L", 160), 4,
+                                                     kw.get("s", 0.1275), None)
+    for s_ in (0.0, -1.0, float("nan"), float("inf")):
+        assert f(s=s_) == 1 and "q_scale" in lib.h3attn_last_error().decode()
+    assert f(q=None) == 1 and f(L=0) == 1 and f(q=A + 8) == 1
+    g = lambda **kw: lib.h3attn_forward_log2(kw.get("q", A), B, C, kw.get("out", O), kw.get("L", 160), 4, None)
+    assert g(q=None) == 1 and g(L=-1) == 1
+    assert g(out=A) == 1 and "overlap" in lib.h3attn_last_error().decode()
 
 
 def test_binding_rejects_bad_tensors_on_cpu():

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from gates import attention_ok, prologue_ok
-from gpu_util import dev_bf16, dev_inputs, head_f64, host_bits, host_f64
+from gpu_util import dev_bf16, dev_inputs, head_f64, host_bits, host_f64, sample_heads, sample_rows
 from packed_full_attention_amd import h3attn_forward, h3attn_qk_prologue
 from packed_full_attention_amd import workloads as wl
 
@@ -41,18 +41,6 @@ def run_prologue(inp):
     h3attn_qk_prologue(q, k, gq, gk, pos)
     torch.cuda.synchronize()
     return q, k, v
-
-
-def sample_rows(w: wl.Workload, n: int, seed: int) -> np.ndarray:
-    L = w.seq_len
-    special = [0, 1, w.n_text - 1, w.n_text, w.n_text + w.n_video - 1, w.n_text + w.n_video,
-               L - 129, L - 128, L - 65, L - 64, L - 2, L - 1]
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([special, rng.choice(L, n, replace=False)])).astype(np.int64)
-
-
-def sample_heads(w: wl.Workload) -> np.ndarray:
-    return np.unique([0, w.heads // 3, (2 * w.heads) // 3, w.heads - 1]).astype(np.int64)
 
 
 # ------------------------------------------------------------------ prologue
