@@ -3,10 +3,11 @@ over the long single-GPU packed document: L = 16500 tokens (256 text +
 36x15x27 video + 1664 audio), H = 56 heads of 128.
 
 The timed step is the scale-folded form of the path: h3attn_qk_prologue_scaled
-(Q's output carries scale * log2(e), applied before its one bf16 rounding) then
-h3attn_forward_log2 (base-2 softmax).  It computes the same attention with the
-same roundings as h3attn_qk_prologue + h3attn_forward, which are timed beside
-it and reported under "plain_path".
+(Q's output carries scale * log2(e), applied before its one bf16 rounding),
+h3attn_v_transpose (V^T, a bit-exact copy) and h3attn_forward_log2 (base-2
+softmax on V^T).  It computes the same attention with the same roundings as
+h3attn_qk_prologue + h3attn_forward, which are timed beside it and reported
+under "plain_path".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
                     [--no-cpu-baseline] [--copy-probe]
@@ -116,7 +117,7 @@ def main() -> int:
     import numpy as np
     import torch
     from packed_full_attention_amd import (h3attn_forward, h3attn_forward_log2, h3attn_qk_prologue,
-                                           h3attn_qk_prologue_scaled, load_library)
+                                           h3attn_qk_prologue_scaled, h3attn_v_transpose, load_library)
     from packed_full_attention_amd import workloads as wl
 
     load_library()
@@ -140,40 +141,41 @@ def main() -> int:
         print(json.dumps({"copy_probe_bytes_read": 256 << 20, "copy_probe_bytes_written": 256 << 20}),
               file=sys.stderr)
 
-    def timed(prologue, forward, K):
-        """Average ms per step, per prologue launch and per forward launch over K steps."""
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    def timed(stages, K):
+        """Average ms per step and per stage launch over K steps."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         start.record(stream)
         for i in range(K):
             ev[i][0].record(stream)
-            prologue()
-            ev[i][1].record(stream)
-            forward()
-            ev[i][2].record(stream)
+            for j, f in enumerate(stages):
+                f()
+                ev[i][j + 1].record(stream)
         stop.record(stream)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3
-        return (start.elapsed_time(stop) / K, sum(e[0].elapsed_time(e[1]) for e in ev) / K,
-                sum(e[1].elapsed_time(e[2]) for e in ev) / K, wall)
+        per = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / K for j in range(len(stages))]
+        return start.elapsed_time(stop) / K, per, wall
 
     stream = torch.cuda.current_stream(dev)
-    pro_s = lambda: h3attn_qk_prologue_scaled(q, k, gq, gk, pos, q_scale)
-    fwd_s = lambda: h3attn_forward_log2(q, k, v, out)
-    pro_p = lambda: h3attn_qk_prologue(q, k, gq, gk, pos)
-    fwd_p = lambda: h3attn_forward(q, k, v, out, scale=scale)
+    vt = torch.empty(H, 128, (L + 63) // 64 * 64, dtype=torch.bfloat16, device=dev)
+    fast = [lambda: h3attn_qk_prologue_scaled(q, k, gq, gk, pos, q_scale),
+            lambda: h3attn_v_transpose(v, vt),
+            lambda: h3attn_forward_log2(q, k, vt, out)]
+    plain = [lambda: h3attn_qk_prologue(q, k, gq, gk, pos),
+             lambda: h3attn_forward(q, k, v, out, scale=scale)]
 
     K = args.steps
     for _ in range(args.warmup):
-        pro_p()
-        fwd_p()
-    plain_ms, plain_pro, plain_att, _ = timed(pro_p, fwd_p, K)
+        for f in plain:
+            f()
+    plain_ms, (plain_pro, plain_att), _ = timed(plain, K)
     for _ in range(args.warmup):
-        pro_s()
-        fwd_s()
-    ms_step, t_pro, t_att, wall_ms = timed(pro_s, fwd_s, K)
+        for f in fast:
+            f()
+    ms_step, (t_pro, t_vt, t_att), wall_ms = timed(fast, K)
     if not bool(torch.isfinite(out.float()).all()):
         print("bench.py: non-finite attention output", file=sys.stderr)
         return 1
@@ -205,6 +207,8 @@ def main() -> int:
         "prologue": {"bound": "hbm", "kernel": "qk_prologue_kernel", "achieved": round(pro_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pro_gbs / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes": prologue_bytes(L, H), "avg_launch_us": round(t_pro * 1e3, 2)},
+        "v_transpose": {"bound": "hbm", "kernel": "v_transpose_kernel", "avg_launch_us": round(t_vt * 1e3, 2),
+                        "achieved": round(2.0 * L * H * 128 * 2 / (t_vt * 1e-3) / 1e9, 1), "unit": "GB/s"},
         "plain_path": {"entry_points": "h3attn_qk_prologue + h3attn_forward", "ms_per_step": round(plain_ms, 4),
                        "attention_ms": round(plain_att, 4),
                        "attention_tflops": round(flops / (plain_att * 1e-3) / 1e12, 2),

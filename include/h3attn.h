@@ -99,29 +99,43 @@ int h3attn_forward(const void* q, const void* k, const void* v, void* out, int64
                    int32_t H, float scale, hipStream_t stream);
 
 /*
- * The same path with the softmax scale folded into q.  Together,
+ * The same path in the layout the fastest kernel reads.  Together,
  *   h3attn_qk_prologue_scaled(q, k, gamma_q, gamma_k, pos_thw, L, H, scale * log2(e), s)
- *   h3attn_forward_log2(q, k, v, out, L, H, s)
+ *   h3attn_v_transpose(v, vt, L, H, s)
+ *   h3attn_forward_log2(q, k, vt, out, L, H, s)
  * compute what h3attn_qk_prologue + h3attn_forward(..., scale, s) compute, with
  * the same single bf16 rounding of q (of the scaled values instead of the
- * unscaled ones); the attention kernel then evaluates each exponential straight
- * from the matrix-core score, without a scaling instruction per score.
+ * unscaled ones).  The attention kernel then evaluates each exponential
+ * straight from the matrix-core score, without a scaling instruction per score,
+ * and reads every P V operand from the transposed V in one 16-byte LDS read.
  *
  * h3attn_qk_prologue_scaled: as h3attn_qk_prologue, except that the Q output
  *   is multiplied by q_scale (finite, > 0; applied in fp32 before the rounding
  *   to bf16).  q_scale = 1 gives h3attn_qk_prologue's output bit for bit.
  *
+ * h3attn_vt_bytes: the size of vt for (L, H): H * 128 * Lp * 2 bytes with
+ *   Lp = L rounded up to a multiple of 64; -1 for an (L, H) the other calls
+ *   reject (L <= 0, H <= 0, L >= 2^31, too large).
+ *
+ * h3attn_v_transpose: vt[h][c][j] = v[j][h][c] for j < L and 0 for
+ *   L <= j < Lp: bf16 [H][128][Lp], caller-owned device memory of
+ *   h3attn_vt_bytes(L, H) bytes, 16-byte aligned, not overlapping v.  A pure
+ *   copy (bit exact).
+ *
  * h3attn_forward_log2: base-2 softmax attention, per head h,
  *   out[i,h,:] = sum_j 2^<q[i,h,:], k[j,h,:]> v[j,h,:] / sum_j 2^<q[i,h,:], k[j,h,:]>
  *   i.e. h3attn_forward with scale = ln 2 (and so, with q from
  *   h3attn_qk_prologue_scaled at q_scale = scale * log2(e), the scale-`scale`
- *   attention of the unscaled q).  Arguments, layouts, ownership and errors as
- *   for h3attn_forward.
+ *   attention of the unscaled q), with V given as vt from h3attn_v_transpose
+ *   (its padding columns must be zero).  q, k, out as for h3attn_forward; out
+ *   must not overlap q, k or vt.
  */
 int h3attn_qk_prologue_scaled(void* q, void* k, const float* gamma_q, const float* gamma_k,
                               const int32_t* pos_thw, int64_t L, int32_t H, float q_scale,
                               hipStream_t stream);
-int h3attn_forward_log2(const void* q, const void* k, const void* v, void* out, int64_t L,
+int64_t h3attn_vt_bytes(int64_t L, int32_t H);
+int h3attn_v_transpose(const void* v, void* vt, int64_t L, int32_t H, hipStream_t stream);
+int h3attn_forward_log2(const void* q, const void* k, const void* vt, void* out, int64_t L,
                         int32_t H, hipStream_t stream);
 
 /* Static description of a status code. */

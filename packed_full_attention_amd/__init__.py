@@ -7,7 +7,8 @@ ctypes binding with the same names as the C entry points, and the seeded
 synthetic workloads.
 """
 from ._binding import (H3AttnError, abi_version, h3attn_forward, h3attn_forward_log2,  # noqa: F401
-                       h3attn_qk_prologue, h3attn_qk_prologue_scaled, load_library, LIB_PATH)
+                       h3attn_qk_prologue, h3attn_qk_prologue_scaled, h3attn_v_transpose, load_library,
+                       padded_length, LIB_PATH)
 
-__all__ = ["h3attn_qk_prologue", "h3attn_forward", "h3attn_qk_prologue_scaled", "h3attn_forward_log2",
-           "abi_version", "load_library", "H3AttnError"]
+__all__ = ["h3attn_qk_prologue", "h3attn_forward", "h3attn_qk_prologue_scaled", "h3attn_v_transpose",
+           "h3attn_forward_log2", "padded_length", "abi_version", "load_library", "H3AttnError"]

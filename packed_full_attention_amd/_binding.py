@@ -17,8 +17,9 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libh3attn.so")
 HEAD_DIM = 128
 H3A_OK, H3A_EINVAL, H3A_EUNSUPPORTED, H3A_EHIP = 0, 1, 2, 3
-EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward", "h3attn_qk_prologue_scaled",
-                    "h3attn_forward_log2", "h3attn_strerror", "h3attn_last_error", "h3attn_abi_version")
+EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward", "h3attn_qk_prologue_scaled", "h3attn_vt_bytes",
+                    "h3attn_v_transpose", "h3attn_forward_log2", "h3attn_strerror", "h3attn_last_error",
+                    "h3attn_abi_version")
 
 _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
@@ -49,6 +50,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.h3attn_qk_prologue_scaled.restype = ctypes.c_int
         lib.h3attn_forward_log2.argtypes = [vp, vp, vp, vp, i64, i32, vp]
         lib.h3attn_forward_log2.restype = ctypes.c_int
+        lib.h3attn_vt_bytes.argtypes = [i64, i32]
+        lib.h3attn_vt_bytes.restype = i64
+        lib.h3attn_v_transpose.argtypes = [vp, vp, i64, i32, vp]
+        lib.h3attn_v_transpose.restype = ctypes.c_int
         lib.h3attn_strerror.argtypes = [ctypes.c_int]
         lib.h3attn_strerror.restype = ctypes.c_char_p
         lib.h3attn_last_error.argtypes = []
@@ -125,7 +130,10 @@ def _forward(fn: str, q, k, v, out, scale):
     dev = q.device
     _check_tensor("q", q, torch.bfloat16, (L, H, HEAD_DIM))
     _check_tensor("k", k, torch.bfloat16, (L, H, HEAD_DIM), dev)
-    _check_tensor("v", v, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    if scale is None:
+        _check_tensor("vt", v, torch.bfloat16, (H, HEAD_DIM, padded_length(L)), dev)
+    else:
+        _check_tensor("v", v, torch.bfloat16, (L, H, HEAD_DIM), dev)
     if out is None:
         out = torch.empty_like(q)
     _check_tensor("out", out, torch.bfloat16, (L, H, HEAD_DIM), dev)
@@ -146,9 +154,31 @@ def h3attn_forward(q, k, v, out=None, scale: Optional[float] = None):
     return _forward("h3attn_forward", q, k, v, out, 1.0 / math.sqrt(HEAD_DIM) if scale is None else scale)
 
 
-def h3attn_forward_log2(q, k, v, out=None):
-    """Base-2 softmax attention (q carries the softmax scale times log2(e)); returns out."""
-    return _forward("h3attn_forward_log2", q, k, v, out, None)
+def padded_length(L: int) -> int:
+    """Lp: L rounded up to a multiple of 64 (the key dimension of vt)."""
+    return (int(L) + 63) // 64 * 64
+
+
+def h3attn_v_transpose(v, vt=None):
+    """vt[h, c, j] = v[j, h, c] for j < L, zero for L <= j < Lp; returns vt (bf16 [H, 128, Lp])."""
+    import torch
+    L, H = _lh(v)
+    dev = v.device
+    _check_tensor("v", v, torch.bfloat16, (L, H, HEAD_DIM))
+    if vt is None:
+        vt = torch.empty(H, HEAD_DIM, padded_length(L), dtype=torch.bfloat16, device=dev)
+    _check_tensor("vt", vt, torch.bfloat16, (H, HEAD_DIM, padded_length(L)), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.h3attn_v_transpose(v.data_ptr(), vt.data_ptr(), L, H, torch.cuda.current_stream(dev).cuda_stream)
+    _raise_on(lib, "h3attn_v_transpose", st)
+    return vt
+
+
+def h3attn_forward_log2(q, k, vt, out=None):
+    """Base-2 softmax attention (q carries the softmax scale times log2(e); V as vt from
+    h3attn_v_transpose); returns out."""
+    return _forward("h3attn_forward_log2", q, k, vt, out, None)
 
 
 def abi_version() -> int:

@@ -127,6 +127,10 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
+// Key held by row r of a K tile (and by S^T accumulator row r) when V comes
+// transposed: bits 2 and 3 of r swapped.
+__device__ __forceinline__ int perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 // ---------------------------------------------------------------- tile DMA
 // A 64-key tile of a [L][H][128] tensor goes into LDS as 16 pieces of 1 KiB;
@@ -142,7 +146,9 @@ struct DmaOffsets {
   uint32_t off[kDmaPerWave];
 };
 
-// Slot (row r, physical chunk p) <- token r of the tile, channels 8 (p ^ swz(r)) .. +7.
+// Row-major tile: slot (row r, physical chunk p) <- token r (token perm(r)
+// with kPerm) of the tile, channels 8 (p ^ swz(r)) .. +7.
+template <bool kPerm>
 __device__ __forceinline__ DmaOffsets dma_offsets(int64_t tok_stride, int wave, int lane) {
   DmaOffsets d;
 #pragma unroll
@@ -150,7 +156,21 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int64_t tok_stride, int wave, 
     const int slot = (it * kWaves + wave) * 64 + lane;  // 16-byte slot in the tile
     const int r = slot >> 4;
     const int c = (slot & 15) ^ swz(r);
-    d.off[it] = (uint32_t)(((int64_t)r * tok_stride + 8 * c) * 2);
+    d.off[it] = (uint32_t)(((int64_t)(kPerm ? perm(r) : r) * tok_stride + 8 * c) * 2);
+  }
+  return d;
+}
+
+// V^T tile (128 channel rows of 64 keys, 128 bytes): slot (row d, physical
+// chunk p) <- channel d, keys 8 (p ^ vswz(d)) .. +7.
+__device__ __forceinline__ DmaOffsets vt_dma_offsets(int64_t vt_row_bytes, int wave, int lane) {
+  DmaOffsets d;
+#pragma unroll
+  for (int it = 0; it < kDmaPerWave; ++it) {
+    const int slot = (it * kWaves + wave) * 64 + lane;
+    const int r = slot >> 3;
+    const int c = (slot & 7) ^ vswz(r);
+    d.off[it] = (uint32_t)(r * vt_row_bytes + 16 * c);
   }
   return d;
 }
@@ -241,7 +261,10 @@ __device__ __forceinline__ bf16x8_t k_operand(int kb, int ks, const lds_char* ld
 // 32 dblk + 16 (G & 1) + 4 (i & 3), and receives keys {16 j + 4 g + e} and
 // {16 j + 8 + 4 g + e} of channel 32 dblk + (l % 32) -- the key order of the
 // P^T accumulator slots.
+template <bool kVT>
 __device__ __forceinline__ bf16x8_t v_operand(int dblk, int j, const lds_char* lds, const Addr& b) {
+  // From a V^T tile: one 16-byte read at row 32 dblk + col, keys 16 j + 8 g .. +7.
+  if (kVT) return *(const lds_bf16x8*)(lds + dblk * 4096 + (b.v0 ^ (32u * j)));
   const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_i16x4*)(lds + 4096 * j + (b.v0 ^ (64u * dblk))));
   const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -250,11 +273,12 @@ __device__ __forceinline__ bf16x8_t v_operand(int dblk, int j, const lds_char* l
 }
 
 // O^T += V_tile^T P^T.
+template <bool kVT>
 __device__ __forceinline__ void pv(State& st, const bf16x8_t (&p)[4], const lds_char* lds, const Addr& b) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int dblk = 0; dblk < 4; ++dblk) st.o[dblk] = mfma32(v_operand(dblk, j, lds, b), p[j], st.o[dblk]);
+    for (int dblk = 0; dblk < 4; ++dblk) st.o[dblk] = mfma32(v_operand<kVT>(dblk, j, lds, b), p[j], st.o[dblk]);
 }
 
 // Weights.  Score n (0..31) of a lane is accumulator slot n % 16 of block
@@ -353,15 +377,19 @@ __device__ __forceinline__ float rebase_log2(const f32x16_t (&s_in)[2], f32x16_t
 }
 
 // Scores of keys at or past L (only in the last, partial tile) become -inf.
-// Accumulator slot 4r + qq of lane half g is key 32 kb + 8 r + 4 g + qq.
+// Accumulator slot 4r + qq of lane half g is tile row 32 kb + 8 r + 4 g + qq,
+// which holds key perm(row) in a permuted K tile.
+template <bool kPerm>
 __device__ __forceinline__ void mask_tail(f32x16_t (&s)[2], int kbase, int L, int g) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        if (kbase + 32 * kb + 8 * r + 4 * g + qq >= L) s[kb][4 * r + qq] = -INFINITY;
+      for (int qq = 0; qq < 4; ++qq) {
+        const int row = 32 * kb + 8 * r + 4 * g + qq;
+        if (kbase + (kPerm ? perm(row) : row) >= L) s[kb][4 * r + qq] = -INFINITY;
+      }
 }
 
 // ---------------------------------------------------------------- kernel
@@ -369,10 +397,11 @@ struct Ctx {
   const lds_char* lds;
   uint32_t lds_base;
   const char* kbase;          // K, this head, token 0
-  const char* vbase;          // V, this head, token 0
-  int64_t tile_bytes;         // 64 tokens of K or V
+  const char* vbase;          // V (row-major: this head, token 0; V^T: this head's first channel row)
+  int64_t tile_bytes;         // 64 tokens of K or row-major V
   int64_t row_bytes;          // one token row of all heads
-  DmaOffsets dma;
+  int64_t vt_valid;           // V^T: bytes from a tile's first byte to its last
+  DmaOffsets kdma, vdma;
   int n_full, n_tiles, L, wave, g;
   float c;
 };
@@ -385,6 +414,15 @@ __device__ __forceinline__ TileDma dma_tile(const Ctx& x, const char* base, int 
   const int64_t valid = (int64_t)(x.L - 1 - t * kBN) * x.row_bytes + kD * 2;
   return tile_dma(base + t * x.tile_bytes, valid, x.lds_base + buf, x.wave);
 }
+// V^T tile t: 64 keys (128 bytes) of each of the head's 128 channel rows.
+__device__ __forceinline__ TileDma dma_vt_tile(const Ctx& x, int t, uint32_t buf) {
+  t = t < x.n_tiles ? t : x.n_tiles - 1;
+  return tile_dma(x.vbase + t * (kBN * 2), x.vt_valid, x.lds_base + buf, x.wave);
+}
+template <bool kVT>
+__device__ __forceinline__ TileDma dma_v(const Ctx& x, int t, uint32_t buf) {
+  return kVT ? dma_vt_tile(x, t, buf) : dma_tile(x, x.vbase, t, buf);
+}
 
 __device__ __forceinline__ uint32_t ring(int t) { return (uint32_t)(t % kStages) * kTileBytes; }
 
@@ -392,9 +430,10 @@ __device__ __forceinline__ uint32_t ring(int t) { return (uint32_t)(t % kStages)
 // slot k is score MFMA k/2 (block kb = (k/2) & 1, k-step ks = k/4), odd slot k
 // is P*V MFMA (k-1)/2 (16-key step j = k/8, d-block (k/2) & 3).  Chains of
 // dependent MFMAs are 4 (scores) or 8 (P*V) slots apart.
+template <bool kVT>
 __device__ __forceinline__ bf16x8_t slot_operand(int k, const lds_char* lds, const Addr& b) {
   const int i = k >> 1;
-  return (k & 1) == 0 ? k_operand(i & 1, i >> 1, lds, b) : v_operand(i & 3, i >> 2, lds, b);
+  return (k & 1) == 0 ? k_operand(i & 1, i >> 1, lds, b) : v_operand<kVT>(i & 3, i >> 2, lds, b);
 }
 
 // Iteration t: S(t+1) from K(t+1) into s_next; O += V(t-1) P(t-1) (skipped for
@@ -413,13 +452,13 @@ __device__ __forceinline__ bf16x8_t slot_operand(int k, const lds_char* lds, con
 // 4x4x4 MFMA that adds two packed pairs to the row sum.  A slot then holds one
 // transcendental and one or two plain VALU instructions next to its 32-cycle
 // matrix instruction; four more slots without one finish the last pairs.
-template <bool kPV, bool kLog2>
+template <bool kPV, bool kLog2, bool kVT>
 __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, const f32x16_t (&s_cur)[2],
                                           f32x16_t (&s_next)[2], const bf16x8_t (&p_prev)[4],
                                           bf16x8_t (&p_cur)[4], int t) {
   asm volatile("" : "+v"(a.k), "+v"(a.v0), "+v"(a.v1));
   const TileDma kd = dma_tile(x, x.kbase, t + 3, ring(t));
-  const TileDma vd = dma_tile(x, x.vbase, t + 1, kVRing + ring(t + 1));
+  const TileDma vd = dma_v<kVT>(x, t + 1, kVRing + ring(t + 1));
   const Addr b = at_buffers(a, ring(t + 1), kVRing + ring(t + 2));
 
   const float c = x.c, mc = st.m * c;
@@ -432,20 +471,20 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     const i16x4_t ones4 = {16256, 16256, 16256, 16256};  // bf16 1.0
     f32x4_t sum4 = {0.f, 0.f, 0.f, 0.f};
     bf16x8_t op[32];
-    op[0] = slot_operand(0, x.lds, b);
-    op[1] = slot_operand(1, x.lds, b);
+    op[0] = slot_operand<kVT>(0, x.lds, b);
+    op[1] = slot_operand<kVT>(1, x.lds, b);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 36; ++k) {
       // This iteration's DMA, one piece every 8 slots: issued all at once by
       // all 8 waves, the loads back up in the address unit and hold the waves
       // at the start of the iteration.
-      if (k == 4) dma_piece(kd, x.dma, 0);
-      if (k == 12) dma_piece(kd, x.dma, 1);
-      if (k == 20) dma_piece(vd, x.dma, 0);
-      if (k == 28) dma_piece(vd, x.dma, 1);
+      if (k == 4) dma_piece(kd, x.kdma, 0);
+      if (k == 12) dma_piece(kd, x.kdma, 1);
+      if (k == 20) dma_piece(vd, x.vdma, 0);
+      if (k == 28) dma_piece(vd, x.vdma, 1);
       if (k < 32) {
-        if (k + 2 < 32) op[k + 2] = slot_operand(k + 2, x.lds, b);
+        if (k + 2 < 32) op[k + 2] = slot_operand<kVT>(k + 2, x.lds, b);
         const int i = k >> 1;
         if ((k & 1) == 0) {
           s_next[i & 1] = mfma32(op[k], st.q[i >> 1], s_next[i & 1]);
@@ -473,8 +512,8 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     store_pairs(w, p_cur);
     psum = sum4[0];
   } else {
-    dma_all(kd, x.dma);
-    dma_all(vd, x.dma);
+    dma_all(kd, x.kdma);
+    dma_all(vd, x.vdma);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
@@ -488,16 +527,16 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
   st.l += psum;
   if (t + 1 >= x.n_full) {
     cold_path();
-    mask_tail(s_next, (t + 1) * kBN, x.L, x.g);
+    mask_tail<kVT>(s_next, (t + 1) * kBN, x.L, x.g);
   }
   dma_wait_all_but<2 * kDmaPerWave>();  // this iteration's DMA may still be in flight
   __syncthreads();  // K(t+2), V(t) landed; every wave is done with K(t+1), V(t-1)
 }
 
-template <bool kLog2>
+template <bool kLog2, bool kVT>
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, int L, int H, float scale_log2e, int n_qtiles) {
+    uint16_t* __restrict__ out, int L, int H, int Lp, float scale_log2e, int n_qtiles) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStages * kTileBytes];
 
   // Workgroups are dispatched round-robin over the 8 XCDs (block b -> XCD b%8).
@@ -526,12 +565,24 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   x.n_tiles = (L + kBN - 1) / kBN;                 // plus one partial tile if L % 64 != 0
   x.tile_bytes = (int64_t)kBN * x.row_bytes;
   x.kbase = reinterpret_cast<const char*>(k + (int64_t)head * kD);
-  x.vbase = reinterpret_cast<const char*>(v + (int64_t)head * kD);
-  x.dma = dma_offsets(tok_stride, x.wave, lane);
+  x.kdma = dma_offsets<kVT>(tok_stride, x.wave, lane);
+  if (kVT) {
+    const int64_t vt_row_bytes = (int64_t)Lp * 2;  // one channel row of V^T
+    x.vbase = reinterpret_cast<const char*>(v + (int64_t)head * kD * Lp);
+    x.vt_valid = (kD - 1) * vt_row_bytes + kBN * 2;
+    x.vdma = vt_dma_offsets(vt_row_bytes, x.wave, lane);
+  } else {
+    x.vbase = reinterpret_cast<const char*>(v + (int64_t)head * kD);
+    x.vt_valid = 0;
+    x.vdma = x.kdma;
+  }
 
   Addr a;
   a.k = 256u * col + ((16u * x.g) ^ (16u * swz(col)));
-  {
+  if (kVT) {
+    a.v0 = 128u * col + 16u * (x.g ^ vswz(col));  // V^T row col, chunk g (XOR 2j per key step)
+    a.v1 = a.v0;
+  } else {
     const int key_a = 4 * (lane >> 5) + ((lane & 15) >> 2);  // transposing-read key of this lane
     const int ch = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // transposing-read channel
     a.v0 = 256u * key_a + 8u * ((ch >> 2) & 1) + ((16u * (ch >> 3)) ^ (16u * swz(key_a)));
@@ -540,8 +591,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
 
   // Ring fill: K(0), K(1), K(2) and V(0).
 #pragma unroll
-  for (int i = 0; i < kStages; ++i) dma_all(dma_tile(x, x.kbase, i, ring(i)), x.dma);
-  dma_all(dma_tile(x, x.vbase, 0, kVRing + ring(0)), x.dma);
+  for (int i = 0; i < kStages; ++i) dma_all(dma_tile(x, x.kbase, i, ring(i)), x.kdma);
+  dma_all(dma_v<kVT>(x, 0, kVRing + ring(0)), x.vdma);
 
   // Q^T operand: lane holds Q[row][16ks + 8g .. +7] for its query row.
   State st;
@@ -572,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s0[kb] = mfma32(k_operand(kb, ks, x.lds, b0), st.q[ks], s0[kb]);
   }
-  if (x.n_full == 0) mask_tail(s0, 0, L, x.g);
+  if (x.n_full == 0) mask_tail<kVT>(s0, 0, L, x.g);
   if (kLog2) {
     // The offset starts at the first tile's row maximum, so no tile needs
     // the -FLT_MAX start (which would swamp the scores held relative to m).
@@ -595,19 +646,19 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   __syncthreads();
 
   // S(t) and P(t) live in s/p[t % 2]; odd/even pairs keep that choice static.
-  iteration<false, kLog2>(x, st, a, s0, s1, p1, p0, 0);
+  iteration<false, kLog2, kVT>(x, st, a, s0, s1, p1, p0, 0);
   int t = 1;
   for (; t + 1 < x.n_tiles; t += 2) {
-    iteration<true, kLog2>(x, st, a, s1, s0, p0, p1, t);
-    iteration<true, kLog2>(x, st, a, s0, s1, p1, p0, t + 1);
+    iteration<true, kLog2, kVT>(x, st, a, s1, s0, p0, p1, t);
+    iteration<true, kLog2, kVT>(x, st, a, s0, s1, p1, p0, t + 1);
   }
   // P(n-1) V(n-1); V(n-1) landed before the last iteration's barrier.
   const Addr b_last = at_buffers(a, 0, kVRing + ring(x.n_tiles - 1));
   if (t < x.n_tiles) {
-    iteration<true, kLog2>(x, st, a, s1, s0, p0, p1, t);
-    pv(st, p1, x.lds, b_last);
+    iteration<true, kLog2, kVT>(x, st, a, s1, s0, p0, p1, t);
+    pv<kVT>(st, p1, x.lds, b_last);
   } else {
-    pv(st, p0, x.lds, b_last);
+    pv<kVT>(st, p0, x.lds, b_last);
   }
   dma_wait();  // the refetches past the end, before the workgroup exits
 
@@ -627,22 +678,75 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   }
 }
 
+// ---------------------------------------------------------------- V transpose
+// vt[h][c][j] = v[j][h][c] for j < L, 0 for L <= j < Lp (Lp = L rounded up
+// to 64): the layout the log2 attention variant reads V in.  One 256-thread
+// workgroup per (64-key block, head): the block's 64 rows x 256 bytes go
+// through LDS (row stride 65 words: the column reads then hit 32 distinct
+// banks), and every 8 consecutive lanes write one 128-byte run of a V^T row.
+constexpr int kVtThreads = 256;
+
+__global__ __launch_bounds__(kVtThreads) void v_transpose_kernel(const uint16_t* __restrict__ v,
+                                                                 uint16_t* __restrict__ vt, int L, int H,
+                                                                 int Lp) {
+  __shared__ uint32_t tile[kBN * 65];
+  const int nblk = Lp / kBN;
+  const int head = blockIdx.x / nblk, key0 = (blockIdx.x - head * nblk) * kBN, tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * kVtThreads + tid, r = idx >> 4, c16 = idx & 15;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (key0 + r < L)
+      val = *reinterpret_cast<const uint4*>(v + ((int64_t)(key0 + r) * H + head) * kD + 8 * c16);
+    uint32_t* dst = tile + r * 65 + 4 * c16;
+    dst[0] = val.x;
+    dst[1] = val.y;
+    dst[2] = val.z;
+    dst[3] = val.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * kVtThreads + tid, d = idx >> 3, c = idx & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = tile[(8 * c + 2 * e) * 65 + (d >> 1)];
+      const uint32_t hi = tile[(8 * c + 2 * e + 1) * 65 + (d >> 1)];
+      w[e] = (d & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    *reinterpret_cast<uint4*>(vt + ((int64_t)head * kD + d) * Lp + key0 + 8 * c) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 }  // namespace
 
 int64_t attention_grid_blocks(int64_t L, int32_t H) { return ((L + kBM - 1) / kBM) * (int64_t)H; }
 int attention_block_threads() { return kThreads; }
+
+int64_t vt_padded_length(int64_t L) { return (L + kBN - 1) / kBN * kBN; }
+int64_t vt_bytes(int64_t L, int32_t H) { return (int64_t)H * kD * vt_padded_length(L) * 2; }
+int64_t transpose_grid_blocks(int64_t L, int32_t H) { return vt_padded_length(L) / kBN * (int64_t)H; }
+int transpose_block_threads() { return kVtThreads; }
+
+hipError_t launch_v_transpose(const uint16_t* v, uint16_t* vt, int64_t L, int32_t H, hipStream_t stream) {
+  hipLaunchKernelGGL(v_transpose_kernel, dim3((unsigned)transpose_grid_blocks(L, H)), dim3(kVtThreads), 0,
+                     stream, v, vt, (int)L, (int)H, (int)vt_padded_length(L));
+  return hipGetLastError();
+}
 
 hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                     uint16_t* out, int64_t L, int32_t H, float scale, bool log2,
                                     hipStream_t stream) {
   const int n_qtiles = (int)((L + kBM - 1) / kBM);
   const dim3 grid((unsigned)attention_grid_blocks(L, H));
-  if (log2)
-    hipLaunchKernelGGL(attention_fwd_kernel<true>, grid, dim3(kThreads), 0, stream, q, k, v, out, (int)L,
-                       (int)H, 1.0f, n_qtiles);
+  if (log2)  // v is V^T
+    hipLaunchKernelGGL((attention_fwd_kernel<true, true>), grid, dim3(kThreads), 0, stream, q, k, v, out,
+                       (int)L, (int)H, (int)vt_padded_length(L), 1.0f, n_qtiles);
   else
-    hipLaunchKernelGGL(attention_fwd_kernel<false>, grid, dim3(kThreads), 0, stream, q, k, v, out, (int)L,
-                       (int)H, scale * kLog2e, n_qtiles);
+    hipLaunchKernelGGL((attention_fwd_kernel<false, false>), grid, dim3(kThreads), 0, stream, q, k, v, out,
+                       (int)L, (int)H, 0, scale * kLog2e, n_qtiles);
   return hipGetLastError();
 }
 

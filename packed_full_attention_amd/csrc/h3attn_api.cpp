@@ -92,10 +92,12 @@ int forward(const void* q, const void* k, const void* v, void* out, int64_t L, i
   uint64_t bytes = 0;
   if (int s = check_shape(L, H, &bytes)) return s;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
-    return fail(H3A_EINVAL, "q, k, v and out must be 16-byte aligned%s");
+    return fail(H3A_EINVAL, log2 ? "q, k, vt and out must be 16-byte aligned%s"
+                                 : "q, k, v and out must be 16-byte aligned%s");
   if (!(isfinite(scale) && scale > 0.0f)) return fail(H3A_EINVAL, "scale must be finite and > 0%s");
-  if (overlap(out, bytes, q, bytes) || overlap(out, bytes, k, bytes) || overlap(out, bytes, v, bytes))
-    return fail(H3A_EINVAL, "out overlaps q, k or v%s");
+  const uint64_t vbytes = log2 ? (uint64_t)h3attn::vt_bytes(L, H) : bytes;
+  if (overlap(out, bytes, q, bytes) || overlap(out, bytes, k, bytes) || overlap(out, bytes, v, vbytes))
+    return fail(H3A_EINVAL, log2 ? "out overlaps q, k or vt%s" : "out overlaps q, k or v%s");
   if (h3attn::attention_grid_blocks(L, H) * h3attn::attention_block_threads() >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "attention grid too large for (L, H)%s");
   const hipError_t e = h3attn::launch_attention_forward(
@@ -106,6 +108,27 @@ int forward(const void* q, const void* k, const void* v, void* out, int64_t L, i
 }
 
 }  // namespace
+
+int64_t h3attn_vt_bytes(int64_t L, int32_t H) {
+  uint64_t bytes = 0;
+  if (check_shape(L, H, &bytes) != H3A_OK) return -1;
+  ok();
+  return h3attn::vt_bytes(L, H);
+}
+
+int h3attn_v_transpose(const void* v, void* vt, int64_t L, int32_t H, hipStream_t stream) {
+  if (!v || !vt) return fail(H3A_EINVAL, "null pointer argument%s");
+  uint64_t bytes = 0;
+  if (int s = check_shape(L, H, &bytes)) return s;
+  if (!aligned(v, 16) || !aligned(vt, 16)) return fail(H3A_EINVAL, "v and vt must be 16-byte aligned%s");
+  if (overlap(vt, (uint64_t)h3attn::vt_bytes(L, H), v, bytes)) return fail(H3A_EINVAL, "vt overlaps v%s");
+  if (h3attn::transpose_grid_blocks(L, H) * h3attn::transpose_block_threads() >= kMaxThreadsPerGrid)
+    return fail(H3A_EUNSUPPORTED, "transpose grid too large for (L, H)%s");
+  const hipError_t e = h3attn::launch_v_transpose(static_cast<const uint16_t*>(v), static_cast<uint16_t*>(vt), L,
+                                                  H, stream);
+  if (e != hipSuccess) return fail(H3A_EHIP, "transpose launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
 
 int h3attn_qk_prologue(void* q, void* k, const float* gamma_q, const float* gamma_k,
                        const int32_t* pos_thw, int64_t L, int32_t H, hipStream_t stream) {
@@ -122,9 +145,9 @@ int h3attn_forward(const void* q, const void* k, const void* v, void* out, int64
   return forward(q, k, v, out, L, H, scale, false, stream);
 }
 
-int h3attn_forward_log2(const void* q, const void* k, const void* v, void* out, int64_t L, int32_t H,
+int h3attn_forward_log2(const void* q, const void* k, const void* vt, void* out, int64_t L, int32_t H,
                         hipStream_t stream) {
-  return forward(q, k, v, out, L, H, 1.0f, true, stream);
+  return forward(q, k, vt, out, L, H, 1.0f, true, stream);
 }
 
 }  // extern "C"

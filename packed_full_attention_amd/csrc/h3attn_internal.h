@@ -14,11 +14,19 @@ hipError_t launch_qk_prologue(uint16_t* q, uint16_t* k, const float* gamma_q,
                               float q_scale, hipStream_t stream);
 
 // Enqueue the flash-attention forward kernel.  log2 = false: weights
-// exp(scale <q,k>); log2 = true: weights 2^<q,k> (q already carries the
-// softmax scale times log2(e)), scale ignored.
+// exp(scale <q,k>), v row-major [L][H][128]; log2 = true: weights 2^<q,k>
+// (q already carries the softmax scale times log2(e)), scale ignored, and v
+// is V^T as written by launch_v_transpose.
 hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                     uint16_t* out, int64_t L, int32_t H, float scale, bool log2,
                                     hipStream_t stream);
+
+// V^T = [H][128][Lp] bf16, Lp = L rounded up to 64, zeros past L.
+hipError_t launch_v_transpose(const uint16_t* v, uint16_t* vt, int64_t L, int32_t H, hipStream_t stream);
+int64_t vt_padded_length(int64_t L);
+int64_t vt_bytes(int64_t L, int32_t H);
+int64_t transpose_grid_blocks(int64_t L, int32_t H);
+int transpose_block_threads();
 
 // Grid size (workgroups) and workgroup size (threads) of the forward launch
 // for (L, H), and the prologue's grid size; used by validation.

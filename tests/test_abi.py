@@ -97,9 +97,23 @@ def test_scaled_entry_points_reject(lib):
     for s_ in (0.0, -1.0, float("nan"), float("inf")):
         assert f(s=s_) == 1 and "q_scale" in lib.h3attn_last_error().decode()
     assert f(q=None) == 1 and f(L=0) == 1 and f(q=A + 8) == 1
-    g = lambda **kw: lib.h3attn_forward_log2(kw.get("q", A), B, C, kw.get("out", O), kw.get("L", 160), 4, None)
-    assert g(q=None) == 1 and g(L=-1) == 1
+    g = lambda **kw: lib.h3attn_forward_log2(kw.get("q", A), B, kw.get("vt", C), kw.get("out", O), kw.get("L", 160),
+                                             4, None)
+    assert g(q=None) == 1 and g(L=-1) == 1 and g(vt=C + 8) == 1
     assert g(out=A) == 1 and "overlap" in lib.h3attn_last_error().decode()
+    # vt is H * 128 * Lp * 2 bytes long, more than v: an out just past v's size still overlaps vt.
+    assert g(out=C + 4 * 128 * 160 * 2) == 1 and "vt" in lib.h3attn_last_error().decode()
+    t = lambda **kw: lib.h3attn_v_transpose(kw.get("v", A), kw.get("vt", B), kw.get("L", 160), 4, None)
+    assert t(v=None) == 1 and t(vt=None) == 1 and t(L=0) == 1 and t(vt=B + 4) == 1
+    assert t(vt=A + 1024) == 1 and "overlap" in lib.h3attn_last_error().decode()
+
+
+@pytest.mark.parametrize("L,H,want", [
+    (160, 4, 4 * 128 * 192 * 2), (64, 1, 128 * 64 * 2), (65, 1, 128 * 128 * 2), (1, 56, 56 * 128 * 64 * 2),
+    (16500, 56, 56 * 128 * 16512 * 2), (0, 4, -1), (160, 0, -1), (1 << 31, 1, -1),
+])
+def test_vt_bytes(lib, L, H, want):
+    assert lib.h3attn_vt_bytes(L, H) == want
 
 
 def test_binding_rejects_bad_tensors_on_cpu():

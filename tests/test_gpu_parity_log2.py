@@ -1,6 +1,7 @@
 """GPU parity of the scale-folded path: h3attn_qk_prologue_scaled (Q output
-times scale * log2(e) before its bf16 rounding) and h3attn_forward_log2
-(base-2 softmax), called through the C ABI, against the fp64 oracle.
+times scale * log2(e) before its bf16 rounding), h3attn_v_transpose (V^T, bit
+exact) and h3attn_forward_log2 (base-2 softmax on V^T), called through the C
+ABI, against the fp64 oracle.
 
 h3attn_forward_log2(q', k, v) is the oracle's attention with scale ln 2 on
 the same bf16 q', k, v; the whole path equals the oracle's packed attention
@@ -16,7 +17,8 @@ import torch
 import oracle
 from gates import attention_ok, prologue_ok
 from gpu_util import dev_bf16, dev_inputs, head_f64, host_bits, host_f64, sample_heads, sample_rows
-from packed_full_attention_amd import (h3attn_forward_log2, h3attn_qk_prologue, h3attn_qk_prologue_scaled)
+from packed_full_attention_amd import (h3attn_forward_log2, h3attn_qk_prologue, h3attn_qk_prologue_scaled,
+                                       h3attn_v_transpose, padded_length)
 from packed_full_attention_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -49,6 +51,37 @@ def run_prologue(inp, kbits=None):
 
 def bf16_of(x: np.ndarray) -> np.ndarray:
     return wl.bf16_bits(x.astype(np.float32))
+
+
+# ------------------------------------------------------------------ V transpose (bit exact)
+
+def transpose_ref(vbits: np.ndarray) -> np.ndarray:
+    L, H, D = vbits.shape
+    ref = np.zeros((H, D, padded_length(L)), np.uint16)
+    ref[:, :, :L] = vbits.transpose(1, 2, 0)
+    return ref
+
+
+@pytest.mark.parametrize("L,H", [(1, 1), (63, 2), (64, 1), (65, 3), (160, 4), (1920, 56), (16500, 56)])
+def test_v_transpose_bit_exact(L, H):
+    vbits = wl.random_document(L, H, seed=40 + L).v
+    vt = h3attn_v_transpose(dev_bf16(vbits))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(vt), transpose_ref(vbits))
+
+
+def test_v_transpose_overwrites_padding_and_stays_in_bounds():
+    # vt starts as NaN patterns in a guarded buffer: padding becomes zero, guards stay.
+    L, H = 70, 2
+    vbits = wl.random_document(L, H, seed=41).v
+    n, guard = H * 128 * padded_length(L), 2048
+    full = dev_bf16(np.full(n + 2 * guard, 0x7FC1, np.uint16))
+    vt = full[guard:guard + n].view(H, 128, padded_length(L))
+    h3attn_v_transpose(dev_bf16(vbits), vt)
+    torch.cuda.synchronize()
+    h = host_bits(full)
+    assert np.all(h[:guard] == 0x7FC1) and np.all(h[-guard:] == 0x7FC1)
+    assert np.array_equal(h[guard:guard + n].reshape(H, 128, -1), transpose_ref(vbits))
 
 
 # ------------------------------------------------------------------ prologue
@@ -101,7 +134,7 @@ def test_forward_log2_parity_full(inputs, idx):
     rq, rk = oracle.qk_prologue(inp.as_f64("q"), inp.as_f64("k"), inp.gamma_q, inp.gamma_k, inp.pos)
     qb, kb = bf16_of(rq * Q_SCALE), bf16_of(rk)
     kb = wl.scale_rows_bf16(kb, inp.stress_rows, 3)
-    out = h3attn_forward_log2(dev_bf16(qb), dev_bf16(kb), dev_bf16(inp.v))
+    out = h3attn_forward_log2(dev_bf16(qb), dev_bf16(kb), h3attn_v_transpose(dev_bf16(inp.v)))
     torch.cuda.synchronize()
     f = lambda b: wl.bf16_bits_to_f32(b).astype(np.float64)
     ref = oracle.attention(f(qb), f(kb), inp.as_f64("v"), LN2)
@@ -115,7 +148,7 @@ def test_forward_log2_parity_sampled_long(inputs, idx):
     # The generated bf16 q (times Q_SCALE, rounded), k, v straight into the kernel.
     inp = inputs(idx)
     qb = bf16_of(wl.bf16_bits_to_f32(inp.q).astype(np.float64) * Q_SCALE)
-    out = h3attn_forward_log2(dev_bf16(qb), dev_bf16(inp.k), dev_bf16(inp.v))
+    out = h3attn_forward_log2(dev_bf16(qb), dev_bf16(inp.k), h3attn_v_transpose(dev_bf16(inp.v)))
     torch.cuda.synchronize()
     rows, heads = sample_rows(inp.workload, 96, 11 + idx), sample_heads(inp.workload)
     got_all = host_bits(out)
@@ -136,7 +169,7 @@ def test_scaled_path_parity_full(inputs, idx):
     inp = inputs(idx)
     kbits = wl.scale_rows_bf16(inp.k, inp.stress_rows, 3)  # literal reading: before the prologue
     q, k, v = run_prologue(inp, kbits)
-    out = h3attn_forward_log2(q, k, v)
+    out = h3attn_forward_log2(q, k, h3attn_v_transpose(v))
     torch.cuda.synchronize()
     kf = wl.bf16_bits_to_f32(kbits).astype(np.float64)
     ref = oracle.packed_attention(inp.as_f64("q"), kf, inp.as_f64("v"), inp.gamma_q, inp.gamma_k,
@@ -150,7 +183,7 @@ def test_scaled_path_parity_full(inputs, idx):
 def test_scaled_path_parity_sampled_long(inputs, idx):
     inp = inputs(idx)
     q, k, v = run_prologue(inp)
-    out = h3attn_forward_log2(q, k, v)
+    out = h3attn_forward_log2(q, k, h3attn_v_transpose(v))
     torch.cuda.synchronize()
     rows, heads = sample_rows(inp.workload, 96, 21 + idx), sample_heads(inp.workload)
     rr = np.repeat(rows[None, :], len(heads), 0).ravel()
@@ -170,7 +203,7 @@ def test_scaled_path_parity_sampled_long(inputs, idx):
 def test_scaled_path_edge_lengths(L, H):
     inp = wl.random_document(L, H, seed=100 + L + H, pos_max=2000)
     q, k, v = run_prologue(inp)
-    out = h3attn_forward_log2(q, k, v)
+    out = h3attn_forward_log2(q, k, h3attn_v_transpose(v))
     torch.cuda.synchronize()
     ref = oracle.packed_attention(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), inp.gamma_q,
                                   inp.gamma_k, inp.pos, SCALE)
@@ -181,7 +214,7 @@ def test_scaled_path_edge_lengths(L, H):
 def test_log2_zero_queries_give_column_mean_of_v():
     inp = wl.random_document(300, 2, seed=5)
     qz = torch.zeros(300, 2, 128, dtype=torch.bfloat16, device="cuda")
-    out = h3attn_forward_log2(qz, dev_bf16(inp.k), dev_bf16(inp.v))
+    out = h3attn_forward_log2(qz, dev_bf16(inp.k), h3attn_v_transpose(dev_bf16(inp.v)))
     torch.cuda.synchronize()
     ref = np.broadcast_to(inp.as_f64("v").mean(axis=0), (300, 2, 128))
     ok, e = attention_ok(host_f64(out), ref)
@@ -193,13 +226,13 @@ def test_scaled_path_repeat_and_head_subset_bit_identical(inputs):
     outs = []
     for _ in range(2):
         q, k, v = run_prologue(inp)
-        outs.append(host_bits(h3attn_forward_log2(q, k, v)))
+        outs.append(host_bits(h3attn_forward_log2(q, k, h3attn_v_transpose(v))))
         torch.cuda.synchronize()
     assert np.array_equal(outs[0], outs[1])
     sub = wl.Inputs(inp.workload, np.ascontiguousarray(inp.q[:, 7:14]), np.ascontiguousarray(inp.k[:, 7:14]),
                     np.ascontiguousarray(inp.v[:, 7:14]), inp.gamma_q, inp.gamma_k, inp.pos, inp.stress_rows)
     q2, k2, v2 = run_prologue(sub)
-    out2 = host_bits(h3attn_forward_log2(q2, k2, v2))
+    out2 = host_bits(h3attn_forward_log2(q2, k2, h3attn_v_transpose(v2)))
     torch.cuda.synchronize()
     assert np.array_equal(outs[0][:, 7:14], out2)
 
@@ -212,7 +245,7 @@ def test_scaled_path_permutation_equivariance(inputs):
     outs = []
     for x in (inp, pinp):
         q, k, v = run_prologue(x)
-        outs.append(host_f64(h3attn_forward_log2(q, k, v)))
+        outs.append(host_f64(h3attn_forward_log2(q, k, h3attn_v_transpose(v))))
     torch.cuda.synchronize()
     ok, e = attention_ok(outs[1], outs[0][perm])
     assert ok, e
@@ -235,7 +268,7 @@ def test_scaled_path_no_writes_outside_buffers():
     out = out_full[guard:guard + n].view(L, H, 128)
     h3attn_qk_prologue_scaled(q, k, torch.from_numpy(inp.gamma_q).cuda(), torch.from_numpy(inp.gamma_k).cuda(),
                               torch.from_numpy(inp.pos).cuda(), Q_SCALE)
-    h3attn_forward_log2(q, k, dev_bf16(inp.v), out)
+    h3attn_forward_log2(q, k, h3attn_v_transpose(dev_bf16(inp.v)), out)
     torch.cuda.synchronize()
     for t in (bufs[0], bufs[1], out_full):
         h = host_bits(t)
