@@ -533,21 +533,49 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
   __syncthreads();  // K(t+2), V(t) landed; every wave is done with K(t+1), V(t-1)
 }
 
+// A wave none of whose 32 query rows exists (only in the last, partial q-tile
+// of a head) still carries its share of the tile DMA and takes part in every
+// barrier, so the other waves see the same ring; it computes nothing, which
+// leaves its SIMD's matrix core to the wave that shares it.
+template <bool kVT>
+__device__ __forceinline__ void stream_only(const Ctx& x) {
+  dma_wait();
+  __syncthreads();  // the ring fill is in LDS
+  __syncthreads();  // the first tile's scores are read
+  for (int t = 0; t < x.n_tiles; ++t) {
+    dma_all(dma_tile(x, x.kbase, t + 3, ring(t)), x.kdma);
+    dma_all(dma_v<kVT>(x, t + 1, kVRing + ring(t + 1)), x.vdma);
+    dma_wait_all_but<2 * kDmaPerWave>();
+    __syncthreads();
+  }
+  dma_wait();
+}
+
 template <bool kLog2, bool kVT>
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, int L, int H, int Lp, float scale_log2e, int n_qtiles) {
+    uint16_t* __restrict__ out, int L, int H, int Lp, float scale_log2e, int n_qfull) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStages * kTileBytes];
 
-  // Workgroups are dispatched round-robin over the 8 XCDs (block b -> XCD b%8).
-  // Renumber so each XCD receives a contiguous run of (head, q-tile) work:
-  // the workgroups that share one head's K/V then share one L2.
-  const int nb = gridDim.x, b = blockIdx.x;
-  const int xcd = b & 7, slot = b >> 3;
-  const int per = nb >> 3, rem = nb & 7;
-  const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  const int head = logical / n_qtiles;
-  const int qtile = logical - head * n_qtiles;
+  // Blocks are dispatched in increasing order, round-robin over the 8 XCDs
+  // (block b -> XCD b % 8).  The first H * n_qfull blocks take the full
+  // 256-row q-tiles, renumbered so that each XCD receives a contiguous run of
+  // them: the workgroups that share one head's K/V then share one L2.  The
+  // last H blocks, dispatched last, take each head's partial q-tile (if L is
+  // not a multiple of 256), which finish sooner (see stream_only) and so fill
+  // the final round of the grid.
+  const int b = blockIdx.x, nfb = H * n_qfull;
+  int head, qtile;
+  if (b < nfb) {
+    const int xcd = b & 7, slot = b >> 3;
+    const int per = nfb >> 3, rem = nfb & 7;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
+    head = logical / n_qfull;
+    qtile = logical - head * n_qfull;
+  } else {
+    head = b - nfb;
+    qtile = n_qfull;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -593,6 +621,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
 #pragma unroll
   for (int i = 0; i < kStages; ++i) dma_all(dma_tile(x, x.kbase, i, ring(i)), x.kdma);
   dma_all(dma_v<kVT>(x, 0, kVRing + ring(0)), x.vdma);
+
+  if (qtile * kBM + x.wave * 32 >= L) {
+    stream_only<kVT>(x);
+    return;
+  }
 
   // Q^T operand: lane holds Q[row][16ks + 8g .. +7] for its query row.
   State st;
@@ -739,14 +772,14 @@ hipError_t launch_v_transpose(const uint16_t* v, uint16_t* vt, int64_t L, int32_
 hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                     uint16_t* out, int64_t L, int32_t H, float scale, bool log2,
                                     hipStream_t stream) {
-  const int n_qtiles = (int)((L + kBM - 1) / kBM);
+  const int n_qfull = (int)(L / kBM);  // full 256-row q-tiles per head
   const dim3 grid((unsigned)attention_grid_blocks(L, H));
   if (log2)  // v is V^T
     hipLaunchKernelGGL((attention_fwd_kernel<true, true>), grid, dim3(kThreads), 0, stream, q, k, v, out,
-                       (int)L, (int)H, (int)vt_padded_length(L), 1.0f, n_qtiles);
+                       (int)L, (int)H, (int)vt_padded_length(L), 1.0f, n_qfull);
   else
     hipLaunchKernelGGL((attention_fwd_kernel<false, false>), grid, dim3(kThreads), 0, stream, q, k, v, out,
-                       (int)L, (int)H, 0, scale * kLog2e, n_qtiles);
+                       (int)L, (int)H, 0, scale * kLog2e, n_qfull);
   return hipGetLastError();
 }
 
