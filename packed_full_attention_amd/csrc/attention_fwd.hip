@@ -35,9 +35,13 @@
 //
 // Key order.  The B operand of a 32x32x16 MFMA takes k-slots 8g .. 8g+7 from
 // lane half g; the P^T operand built from S^T accumulator rows holds, in those
-// slots, keys 16j + {4g .. 4g+3, 8+4g .. 11+4g}.  The V^T operand is gathered
-// from the row-major V tile in that same key order by two transposing LDS
-// reads (ds_read_b64_tr_b16), so no data is reordered anywhere.
+// slots, keys 16j + {4g .. 4g+3, 8+4g .. 11+4g}.  The plain variant gathers the
+// V^T operand from the row-major V tile in that same key order by two
+// transposing LDS reads (ds_read_b64_tr_b16).  The log2 variant reads V
+// transposed ([H][128][Lp] in memory, so a tile is 128 channel rows of 64 keys)
+// with one 16-byte read of 8 consecutive keys, and permutes the rows of its K
+// tile instead (bits 2 and 3 of the row index swapped), which makes the P^T
+// slots of a lane half hold consecutive keys.  No data is reordered anywhere.
 //
 // Software pipeline.  Iteration t issues
 //   S(t+1) = K(t+1) Q^T        (matrix cores)
@@ -48,31 +52,37 @@
 // instruction runs for 32 cycles, during which the same SIMD executes about
 // three independent VALU instructions of this or of the other wave at no cost.
 //
-// LDS.  Two rings of three 16 KiB tiles, K and V: during iteration t the
-// waves read K(t+1) and V(t-1) while DMA (buffer_load_dwordx4 ... lds, no
-// VGPR staging) fills K(t+3) and V(t+1), each into the slot its ring freed in
-// iteration t-1; one barrier per tile, and a DMA has two iterations to land.
-// The DMA is issued by inline asm and awaited explicitly (vmcnt) before each
-// tile barrier: the compiler, which cannot prove that the in-flight writes miss
-// the buffers being read, would otherwise wait for them before every LDS read.
-// Both tiles are stored row-major (one 256-byte row per key, sixteen 16-byte
-// chunks), chunk c of row r at physical chunk c ^ swz(r),
-// swz(r) = 4 (r & 3) + ((r >> 2) & 3).  The LDS has 64 four-byte banks and
-// serves 16 lanes of a 16-byte read, or 32 lanes of an 8-byte read, per cycle;
-// swz takes 16 distinct values over any 16 consecutive rows (the K operand
-// read) and distinct top bits over 4 consecutive rows (the transposing V read:
-// 32 lanes = 4 keys x 4 chunks), so both are conflict-free (checked with the
-// SQ_LDS_BANK_CONFLICT counter).
+// LDS.  Two rings of four 16 KiB tiles, K and V (128 KiB): during iteration t
+// the waves read K(t+1) and V(t-1) while DMA (buffer_load_dwordx4 ... lds, no
+// VGPR staging) fills K(t+4) and V(t+2), each into the slot its ring freed in
+// iteration t-1; one barrier per tile, and a DMA has about two iterations to
+// land.  The DMA is issued by inline asm and awaited explicitly (vmcnt) before
+// each tile barrier: the compiler, which cannot prove that the in-flight writes
+// miss the buffers being read, would otherwise wait for them before every LDS
+// read.  Row-major tiles (one 256-byte row per key, sixteen 16-byte chunks)
+// put chunk c of row r at physical chunk c ^ swz(r),
+// swz(r) = 4 (r & 3) + ((r >> 2) & 3); V^T tiles (128-byte rows) put chunk c
+// of row d at c ^ ((d >> 1) & 7).  The LDS has 64 four-byte banks and serves
+// 16 lanes of a 16-byte read, or 32 lanes of an 8-byte read, per cycle; both
+// swizzles spread each read over all banks, so every operand read is
+// conflict-free (checked with the SQ_LDS_BANK_CONFLICT counter).
 //
 // Exponent offset.  The weights of a tile are computed against the offset m
 // the row already has, with no per-tile maximum.  Each lane adds up the bf16
 // weights it produced (exactly the values that enter the P*V product, so O / l
-// does not depend on m).  If some lane's sum
+// does not depend on m; a sum of the fp32 weights before rounding would not
+// cancel their rounding when a few keys dominate a row).  If some lane's sum
 // exceeds 2^8 (so some weight may exceed 2^8, or overflowed), the wave takes a
 // rare path: m moves to the row maximum of the tile, the already accumulated O
-// and l are scaled by 2^(c (m_old - m_new)), and the tile's weights are
-// recomputed.  m starts at -FLT_MAX, so the first tile always takes that path.
-// Every weight that reaches the matrix cores is therefore at most 2^8.
+// and l are scaled by 2^(m_old - m_new) in exponent units, and the tile's
+// weights are recomputed.  Every weight that reaches the matrix cores is
+// therefore at most 2^8.  The plain variant starts m at -FLT_MAX, so its first
+// tile always takes that path; the log2 variant starts m at the first tile's
+// row maximum.
+//
+// Grid order.  Each head's partial last q-tile (L not a multiple of 256) is
+// dispatched last, and its waves that own no query row only carry their share
+// of the DMA, so those shorter workgroups fill the grid's final round.
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <stdint.h>
@@ -99,7 +109,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kDmaPerWave = 16 / kWaves;  // 1 KiB DMA pieces per wave per tile
 static_assert(kDmaPerWave == 2, "the slot loop issues two K and two V pieces per wave");
 constexpr int kTileBytes = kBN * kD * 2;  // 16 KiB per K or V tile
-constexpr int kStages = 3;                // tiles per ring (resident or in flight)
+constexpr int kStages = 4;                // tiles per ring (resident or in flight)
 constexpr int kVRing = kStages * kTileBytes;  // the V ring follows the K ring
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSumBound = 256.0f;        // a lane's tile sum of P above this moves the offset
@@ -437,12 +447,13 @@ __device__ __forceinline__ bf16x8_t slot_operand(int k, const lds_char* lds, con
 }
 
 // Iteration t: S(t+1) from K(t+1) into s_next; O += V(t-1) P(t-1) (skipped for
-// t = 0); P(t) from s_cur into p_cur.  K(t+1) sits in ring slot (t+1) % 3 and
-// V(t-1) in slot (t-1) % 3.  DMA fills K(t+3) into the K slot of K(t) (read in
-// iteration t-1) and V(t+1) into the V slot of V(t-2) (read in iteration t-1);
-// the previous iteration's DMA (K(t+2), V(t)) must have landed before the
-// barrier that ends this one.  In the last iteration there
-// is no K(t+1): S(t+1) is computed from a stale slot and never used.
+// t = 0); P(t) from s_cur into p_cur.  K(t+1) sits in ring slot (t+1) % 4 and
+// V(t-1) in slot (t-1) % 4.  DMA fills K(t+4) into the K slot of K(t) (read in
+// iteration t-1) and V(t+2) into the V slot of V(t-2) (read in iteration t-1);
+// the DMA of iteration t-2 (K(t+2), V(t)) must have landed before the barrier
+// that ends this one, so each DMA has about two iterations to arrive.  In the
+// last iteration there is no K(t+1): S(t+1) is computed from a stale slot and
+// never used.
 //
 // With the P*V product (t > 0) the instruction order is fixed by hand, slot by
 // slot, with scheduling barriers in between: the operand read of slot k + 2,
@@ -457,9 +468,9 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
                                           f32x16_t (&s_next)[2], const bf16x8_t (&p_prev)[4],
                                           bf16x8_t (&p_cur)[4], int t) {
   asm volatile("" : "+v"(a.k), "+v"(a.v0), "+v"(a.v1));
-  const TileDma kd = dma_tile(x, x.kbase, t + 3, ring(t));
-  const TileDma vd = dma_v<kVT>(x, t + 1, kVRing + ring(t + 1));
-  const Addr b = at_buffers(a, ring(t + 1), kVRing + ring(t + 2));
+  const TileDma kd = dma_tile(x, x.kbase, t + kStages, ring(t));
+  const TileDma vd = dma_v<kVT>(x, t + kStages - 2, kVRing + ring(t + kStages - 2));
+  const Addr b = at_buffers(a, ring(t + 1), kVRing + ring(t + kStages - 1));
 
   const float c = x.c, mc = st.m * c;
   float psum;
@@ -529,7 +540,7 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     cold_path();
     mask_tail<kVT>(s_next, (t + 1) * kBN, x.L, x.g);
   }
-  dma_wait_all_but<2 * kDmaPerWave>();  // this iteration's DMA may still be in flight
+  dma_wait_all_but<(kStages - 2) * 2 * kDmaPerWave>();  // the last two iterations' DMA may be in flight
   __syncthreads();  // K(t+2), V(t) landed; every wave is done with K(t+1), V(t-1)
 }
 
@@ -543,9 +554,9 @@ __device__ __forceinline__ void stream_only(const Ctx& x) {
   __syncthreads();  // the ring fill is in LDS
   __syncthreads();  // the first tile's scores are read
   for (int t = 0; t < x.n_tiles; ++t) {
-    dma_all(dma_tile(x, x.kbase, t + 3, ring(t)), x.kdma);
-    dma_all(dma_v<kVT>(x, t + 1, kVRing + ring(t + 1)), x.vdma);
-    dma_wait_all_but<2 * kDmaPerWave>();
+    dma_all(dma_tile(x, x.kbase, t + kStages, ring(t)), x.kdma);
+    dma_all(dma_v<kVT>(x, t + kStages - 2, kVRing + ring(t + kStages - 2)), x.vdma);
+    dma_wait_all_but<(kStages - 2) * 2 * kDmaPerWave>();
     __syncthreads();
   }
   dma_wait();
@@ -617,10 +628,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     a.v1 = 256u * (8 + key_a) + 8u * ((ch >> 2) & 1) + ((16u * (ch >> 3)) ^ (16u * swz(8 + key_a)));
   }
 
-  // Ring fill: K(0), K(1), K(2) and V(0).
+  // Ring fill: K(0) .. K(3), V(0) and V(1).
 #pragma unroll
   for (int i = 0; i < kStages; ++i) dma_all(dma_tile(x, x.kbase, i, ring(i)), x.kdma);
-  dma_all(dma_v<kVT>(x, 0, kVRing + ring(0)), x.vdma);
+#pragma unroll
+  for (int i = 0; i < kStages - 2; ++i) dma_all(dma_v<kVT>(x, i, kVRing + ring(i)), x.vdma);
 
   if (qtile * kBM + x.wave * 32 >= L) {
     stream_only<kVT>(x);
