@@ -22,7 +22,10 @@
 // channels 96..127.  The sum of squares is a 16-lane butterfly.  A lane's
 // four angles depend only on the token, so their sines and cosines are
 // computed once per token and reused for all 2H head-rows (Q then K) the wave
-// walks through, 32 rows (eight 4-row passes) in flight at a time.
+// walks through in chunks of kPasses 4-row passes whose loads are all in flight
+// together; kPasses is chosen per H so the chunks waste the fewest row slots
+// (14 passes = 56 rows for H = 56: each chunk is exactly one tensor's rows of
+// the token).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,7 +36,6 @@ namespace {
 
 constexpr int kHeadDim = 128;
 constexpr int kWavesPerBlock = 4;     // one token per wave
-constexpr int kPassesPerChunk = 8;    // 8 passes x 4 rows = 32 rows in flight per wave
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -46,6 +48,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+template <int kPassesPerChunk>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
     uint16_t* __restrict__ q, uint16_t* __restrict__ k, const float* __restrict__ gamma_q,
     const float* __restrict__ gamma_k, const int32_t* __restrict__ pos, int64_t L, int32_t H,
@@ -135,11 +138,33 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
 
 int64_t prologue_grid_blocks(int64_t L) { return (L + kWavesPerBlock - 1) / kWavesPerBlock; }
 
+// Passes per chunk for 2H rows: the candidate whose chunks leave the fewest
+// row slots empty, the larger on a tie.
+static int prologue_passes(int32_t H) {
+  const int candidates[3] = {14, 8, 4};
+  int best = 14;
+  int64_t best_waste = -1;
+  for (int p : candidates) {
+    const int64_t rows = 4 * p, waste = (2 * (int64_t)H + rows - 1) / rows * rows - 2 * (int64_t)H;
+    if (best_waste < 0 || waste < best_waste) best = p, best_waste = waste;
+  }
+  return best;
+}
+
 hipError_t launch_qk_prologue(uint16_t* q, uint16_t* k, const float* gamma_q, const float* gamma_k,
                               const int32_t* pos, int64_t L, int32_t H, float q_scale, hipStream_t stream) {
-  const dim3 grid((unsigned)prologue_grid_blocks(L));
-  hipLaunchKernelGGL(qk_prologue_kernel, grid, dim3(kWavesPerBlock * 64), 0, stream, q, k, gamma_q,
-                     gamma_k, pos, L, H, q_scale);
+  const dim3 grid((unsigned)prologue_grid_blocks(L)), block(kWavesPerBlock * 64);
+  switch (prologue_passes(H)) {
+    case 14:
+      hipLaunchKernelGGL(qk_prologue_kernel<14>, grid, block, 0, stream, q, k, gamma_q, gamma_k, pos, L, H, q_scale);
+      break;
+    case 8:
+      hipLaunchKernelGGL(qk_prologue_kernel<8>, grid, block, 0, stream, q, k, gamma_q, gamma_k, pos, L, H, q_scale);
+      break;
+    default:
+      hipLaunchKernelGGL(qk_prologue_kernel<4>, grid, block, 0, stream, q, k, gamma_q, gamma_k, pos, L, H, q_scale);
+      break;
+  }
   return hipGetLastError();
 }
 
