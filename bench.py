@@ -39,6 +39,7 @@ METRIC = "packed-attention TFLOP/s + % bf16 MFMA peak at L~16.5k, H=56; prologue
 # MI355X (gfx950) published peaks: 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU; HBM3E 8 TB/s.
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
+MAX_STEPS = 256  # warm-up + timed steps, each with its own q/k copy (473 MiB at L=16500, H=56)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -68,6 +69,22 @@ def measured_traffic(L: int, H: int):
     if not sha or not val or sha.group(1) != kernel_source_sha():
         return None
     return float(val.group(1))
+
+
+def measured_mfma(L: int, H: int):
+    """MFMA-busy percentage and effective shader clock of the attention kernel from
+    the committed counter summary, or (None, None) when it is absent or was taken
+    on a different kernel source."""
+    path = os.path.join(PROFILES, f"attention_fwd_L{L}_H{H}_mfma_util.md")
+    if not os.path.exists(path):
+        return None, None
+    txt = open(path).read()
+    sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    busy = re.search(r"mfma_busy_pct:\s*([0-9.]+)", txt)
+    clk = re.search(r"effective_sclk_mhz:\s*([0-9.]+)", txt)
+    if not sha or not busy or sha.group(1) != kernel_source_sha():
+        return None, None
+    return float(busy.group(1)), (float(clk.group(1)) if clk else None)
 
 
 def cpu_baseline(inp, L: int, H: int, budget_s: float = 12.0) -> dict:
@@ -141,8 +158,9 @@ def main() -> int:
         print(json.dumps({"copy_probe_bytes_read": 256 << 20, "copy_probe_bytes_written": 256 << 20}),
               file=sys.stderr)
 
-    def timed(stages, K):
-        """Average ms per step and per stage launch over K steps."""
+    def timed(stages, K, first=0):
+        """Average ms per step and per stage launch over steps first .. first+K-1;
+        stage j of step i is stages[j](i)."""
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -151,7 +169,7 @@ def main() -> int:
         for i in range(K):
             ev[i][0].record(stream)
             for j, f in enumerate(stages):
-                f()
+                f(first + i)
                 ev[i][j + 1].record(stream)
         stop.record(stream)
         torch.cuda.synchronize()
@@ -161,29 +179,65 @@ def main() -> int:
 
     stream = torch.cuda.current_stream(dev)
     vt = torch.empty(H, 128, (L + 63) // 64 * 64, dtype=torch.bfloat16, device=dev)
-    fast = [lambda: h3attn_qk_prologue_scaled(q, k, gq, gk, pos, q_scale),
-            lambda: h3attn_v_transpose(v, vt),
-            lambda: h3attn_forward_log2(q, k, vt, out)]
-    plain = [lambda: h3attn_qk_prologue(q, k, gq, gk, pos),
-             lambda: h3attn_forward(q, k, v, out, scale=scale)]
+    K, W = args.steps, args.warmup
+    # The prologue rewrites q and k in place, so every step gets its own copy of
+    # the generated inputs (made before timing): a step never sees the output of
+    # an earlier one.  (Fed back, the per-channel gammas compound step after step
+    # and the scores drift away from the workload's distribution.)
+    if K + W > MAX_STEPS:
+        print(f"bench.py: --steps + --warmup must be <= {MAX_STEPS} (each step holds its own "
+              f"{2 * q.numel() * 2 / 2**20:.0f} MiB copy of q and k)", file=sys.stderr)
+        return 2
+    qs = [torch.empty_like(q) for _ in range(K + W)]
+    ks = [torch.empty_like(k) for _ in range(K + W)]
 
-    K = args.steps
-    for _ in range(args.warmup):
+    def refresh():
+        for a, b in zip(qs, ks):
+            a.copy_(q)
+            b.copy_(k)
+        torch.cuda.synchronize()
+
+    fast = [lambda i: h3attn_qk_prologue_scaled(qs[i], ks[i], gq, gk, pos, q_scale),
+            lambda i: h3attn_v_transpose(v, vt),
+            lambda i: h3attn_forward_log2(qs[i], ks[i], vt, out)]
+    plain = [lambda i: h3attn_qk_prologue(qs[i], ks[i], gq, gk, pos),
+             lambda i: h3attn_forward(qs[i], ks[i], v, out, scale=scale)]
+
+    refresh()
+    for i in range(W):
         for f in plain:
-            f()
-    plain_ms, (plain_pro, plain_att), _ = timed(plain, K)
-    for _ in range(args.warmup):
+            f(i)
+    plain_ms, (plain_pro, plain_att), _ = timed(plain, K, W)
+    refresh()
+    for i in range(W):
         for f in fast:
-            f()
-    ms_step, (t_pro, t_vt, t_att), wall_ms = timed(fast, K)
+            f(i)
+    ms_step, (t_pro, t_vt, t_att), wall_ms = timed(fast, K, W)
+    del qs, ks
     if not bool(torch.isfinite(out.float()).all()):
         print("bench.py: non-finite attention output", file=sys.stderr)
         return 1
+
+    # Reference for the prologue: a device-to-device copy (torch's copy kernel) that
+    # moves the same bytes, Q and K sized, read once and written once.
+    src = torch.zeros(2 * L * H * 128, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * src.numel() * 2 / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+    del src, dst
 
     flops = attention_flops(L, H)
     att_tflops = flops / (t_att * 1e-3) / 1e12
     pro_gbs = prologue_bytes(L, H) / (t_pro * 1e-3) / 1e9
     traffic = measured_traffic(L, H)
+    mfma_busy, sclk = measured_mfma(L, H)
     result = {
         "metric": METRIC,
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
@@ -203,10 +257,11 @@ def main() -> int:
         "roofline": {"bound": "mfma", "kernel": "attention_fwd_kernel<log2>", "achieved": round(att_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "avg_launch_ms": round(t_att, 4)},
+                     "avg_launch_ms": round(t_att, 4), "mfma_busy_pct": mfma_busy, "sclk_mhz": sclk},
         "prologue": {"bound": "hbm", "kernel": "qk_prologue_kernel", "achieved": round(pro_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pro_gbs / PEAK_HBM_GBS, 4),
-                     "algorithmic_bytes": prologue_bytes(L, H), "avg_launch_us": round(t_pro * 1e3, 2)},
+                     "algorithmic_bytes": prologue_bytes(L, H), "avg_launch_us": round(t_pro * 1e3, 2),
+                     "copy_reference_gbs": round(copy_gbs, 1), "frac_of_copy": round(pro_gbs / copy_gbs, 4)},
         "v_transpose": {"bound": "hbm", "kernel": "v_transpose_kernel", "avg_launch_us": round(t_vt * 1e3, 2),
                         "achieved": round(2.0 * L * H * 128 * 2 / (t_vt * 1e-3) / 1e9, 1), "unit": "GB/s"},
         "plain_path": {"entry_points": "h3attn_qk_prologue + h3attn_forward", "ms_per_step": round(plain_ms, 4),
