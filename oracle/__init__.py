@@ -2,3 +2,6 @@
 from .h3_oracle import *  # noqa: F401,F403
 from .h3_oracle import (HEAD_DIM, ROTARY_DIM, HALF, FREQS_PER_AXIS, ROPE_THETA,  # noqa: F401
                         RMS_EPS)
+from .h3_oracle_backward import (attention_head_backward, attention_backward,  # noqa: F401
+                                 log_sum_exp_rows, mm_rope_backward, rms_norm_backward,
+                                 qk_prologue_backward, packed_attention_backward)
