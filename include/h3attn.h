@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 2
+#define H3ATTN_ABI_VERSION 3
 #define H3ATTN_HEAD_DIM 128
 
 /* Status codes. */
@@ -137,6 +137,54 @@ int64_t h3attn_vt_bytes(int64_t L, int32_t H);
 int h3attn_v_transpose(const void* v, void* vt, int64_t L, int32_t H, hipStream_t stream);
 int h3attn_forward_log2(const void* q, const void* k, const void* vt, void* out, int64_t L,
                         int32_t H, hipStream_t stream);
+
+/*
+ * Training: the backward pass ("MiniMax-H3 WS1/WS2 kernel roadmap" RFC,
+ * section 7, per-operator gate: forward and backward of each operator).
+ *
+ * h3attn_forward_lse: h3attn_forward, and in addition
+ *   lse[h*L + i] = ln( sum_j exp( scale * <q[i,h,:], k[j,h,:]> ) )
+ *   fp32 [H][L], 4-byte aligned, not overlapping q, k, v or out.
+ *
+ * h3attn_attention_backward: given dout = dLoss/dout of that forward, with
+ *   P = softmax(scale Q K^T) per head (recomputed from lse), O = out,
+ *     dv = P^T dout
+ *     dS = P * (dout V^T - delta),  delta_i = <dout_i, out_i>
+ *     dq = scale dS K,  dk = scale dS^T Q
+ *   q, k, v, out, dout: bf16 [L][H][128] (q, k as passed to the forward,
+ *   i.e. after the prologue); lse: that forward's lse; dq, dk, dv: bf16
+ *   [L][H][128] outputs (fp32 accumulation, one rounding); workspace:
+ *   caller-owned device memory of h3attn_attention_backward_workspace_bytes(L, H)
+ *   bytes (it receives delta, fp32 [H][L]).  All 16-byte aligned (lse, the
+ *   workspace: 4); the outputs and the workspace must not overlap one another
+ *   or any input.  Three launches on `stream`; deterministic (no atomics, no
+ *   split: one wave produces each output row).
+ *
+ * h3attn_qk_prologue_backward: given dq, dk = the gradients with respect to
+ *   the prologue's outputs, overwrites them (in place) with the gradients with
+ *   respect to its inputs q, k, and writes the gamma gradients:
+ *     dy = inverse rotation of the output gradient (RoPE^T)
+ *     dx = r (gamma dy) - x r^3 mean(gamma dy x),  r = (mean(x^2) + 1e-5)^(-1/2)
+ *     dgamma[c] = sum over every token and head of dy_c x_c r
+ *   q, k: the prologue's raw inputs (bf16 [L][H][128], not modified; keep a
+ *   copy, since h3attn_qk_prologue rewrites them); gamma_q, gamma_k, pos_thw
+ *   as for h3attn_qk_prologue; dq, dk bf16 [L][H][128], in place; dgamma_q,
+ *   dgamma_k fp32 [128]; workspace: h3attn_qk_prologue_backward_workspace_bytes(L, H)
+ *   bytes.  The gamma sums are added in a fixed order (deterministic).
+ *
+ * The *_workspace_bytes calls return -1 for an (L, H) the others reject.
+ */
+int h3attn_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse, int64_t L,
+                       int32_t H, float scale, hipStream_t stream);
+int64_t h3attn_attention_backward_workspace_bytes(int64_t L, int32_t H);
+int h3attn_attention_backward(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              void* workspace, int64_t L, int32_t H, float scale, hipStream_t stream);
+int64_t h3attn_qk_prologue_backward_workspace_bytes(int64_t L, int32_t H);
+int h3attn_qk_prologue_backward(const void* q, const void* k, const float* gamma_q, const float* gamma_k,
+                                const int32_t* pos_thw, void* dq, void* dk, float* dgamma_q,
+                                float* dgamma_k, void* workspace, int64_t L, int32_t H,
+                                hipStream_t stream);
 
 /* Static description of a status code. */
 const char* h3attn_strerror(int status);

@@ -18,8 +18,10 @@ LIB_PATH = os.path.join(PKG_DIR, "libh3attn.so")
 HEAD_DIM = 128
 H3A_OK, H3A_EINVAL, H3A_EUNSUPPORTED, H3A_EHIP = 0, 1, 2, 3
 EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward", "h3attn_qk_prologue_scaled", "h3attn_vt_bytes",
-                    "h3attn_v_transpose", "h3attn_forward_log2", "h3attn_strerror", "h3attn_last_error",
-                    "h3attn_abi_version")
+                    "h3attn_v_transpose", "h3attn_forward_log2", "h3attn_forward_lse",
+                    "h3attn_attention_backward_workspace_bytes", "h3attn_attention_backward",
+                    "h3attn_qk_prologue_backward_workspace_bytes", "h3attn_qk_prologue_backward",
+                    "h3attn_strerror", "h3attn_last_error", "h3attn_abi_version")
 
 _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
@@ -54,6 +56,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.h3attn_vt_bytes.restype = i64
         lib.h3attn_v_transpose.argtypes = [vp, vp, i64, i32, vp]
         lib.h3attn_v_transpose.restype = ctypes.c_int
+        lib.h3attn_forward_lse.argtypes = [vp, vp, vp, vp, vp, i64, i32, ctypes.c_float, vp]
+        lib.h3attn_forward_lse.restype = ctypes.c_int
+        lib.h3attn_attention_backward_workspace_bytes.argtypes = [i64, i32]
+        lib.h3attn_attention_backward_workspace_bytes.restype = i64
+        lib.h3attn_attention_backward.argtypes = [vp] * 10 + [i64, i32, ctypes.c_float, vp]
+        lib.h3attn_attention_backward.restype = ctypes.c_int
+        lib.h3attn_qk_prologue_backward_workspace_bytes.argtypes = [i64, i32]
+        lib.h3attn_qk_prologue_backward_workspace_bytes.restype = i64
+        lib.h3attn_qk_prologue_backward.argtypes = [vp] * 10 + [i64, i32, vp]
+        lib.h3attn_qk_prologue_backward.restype = ctypes.c_int
         lib.h3attn_strerror.argtypes = [ctypes.c_int]
         lib.h3attn_strerror.restype = ctypes.c_char_p
         lib.h3attn_last_error.argtypes = []
@@ -179,6 +191,88 @@ def h3attn_forward_log2(q, k, vt, out=None):
     """Base-2 softmax attention (q carries the softmax scale times log2(e); V as vt from
     h3attn_v_transpose); returns out."""
     return _forward("h3attn_forward_log2", q, k, vt, out, None)
+
+
+def h3attn_forward_lse(q, k, v, out=None, lse=None, scale: Optional[float] = None):
+    """h3attn_forward that also returns each row's natural log-sum-exp, fp32 [H, L]:
+    returns (out, lse)."""
+    import torch
+    L, H = _lh(q)
+    dev = q.device
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty(H, L, dtype=torch.float32, device=dev) if lse is None else lse
+    _check_tensor("out", out, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    _check_tensor("lse", lse, torch.float32, (H, L), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.h3attn_forward_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), L, H,
+                                    scale, torch.cuda.current_stream(dev).cuda_stream)
+    _raise_on(lib, "h3attn_forward_lse", st)
+    return out, lse
+
+
+def h3attn_attention_backward(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, workspace=None,
+                              scale: Optional[float] = None):
+    """Gradients (dq, dk, dv), bf16 [L, H, 128], of h3attn_forward_lse's output given dout."""
+    import torch
+    L, H = _lh(q)
+    dev = q.device
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_tensor(name, t, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    _check_tensor("lse", lse, torch.float32, (H, L), dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    lib = load_library()
+    nbytes = int(lib.h3attn_attention_backward_workspace_bytes(L, H))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.numel() * workspace.element_size() < nbytes or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous buffer of >= {nbytes} bytes on {dev}")
+    with torch.cuda.device(dev):
+        st = lib.h3attn_attention_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                           workspace.data_ptr(), L, H, scale,
+                                           torch.cuda.current_stream(dev).cuda_stream)
+    _raise_on(lib, "h3attn_attention_backward", st)
+    return dq, dk, dv
+
+
+def h3attn_qk_prologue_backward(q, k, gamma_q, gamma_k, pos_thw, dq, dk, dgamma_q=None, dgamma_k=None,
+                                workspace=None):
+    """In place: dq, dk (gradients w.r.t. the prologue outputs) become the gradients w.r.t. the
+    raw q, k; returns (dgamma_q, dgamma_k), fp32 [128]."""
+    import torch
+    L, H = _lh(q)
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("dq", dq), ("dk", dk)):
+        _check_tensor(name, t, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    _check_tensor("gamma_q", gamma_q, torch.float32, (HEAD_DIM,), dev)
+    _check_tensor("gamma_k", gamma_k, torch.float32, (HEAD_DIM,), dev)
+    _check_tensor("pos_thw", pos_thw, torch.int32, (L, 3), dev)
+    dgamma_q = torch.empty(HEAD_DIM, dtype=torch.float32, device=dev) if dgamma_q is None else dgamma_q
+    dgamma_k = torch.empty(HEAD_DIM, dtype=torch.float32, device=dev) if dgamma_k is None else dgamma_k
+    _check_tensor("dgamma_q", dgamma_q, torch.float32, (HEAD_DIM,), dev)
+    _check_tensor("dgamma_k", dgamma_k, torch.float32, (HEAD_DIM,), dev)
+    lib = load_library()
+    nbytes = int(lib.h3attn_qk_prologue_backward_workspace_bytes(L, H))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.numel() * workspace.element_size() < nbytes or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous buffer of >= {nbytes} bytes on {dev}")
+    with torch.cuda.device(dev):
+        st = lib.h3attn_qk_prologue_backward(q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(),
+                                             pos_thw.data_ptr(), dq.data_ptr(), dk.data_ptr(), dgamma_q.data_ptr(),
+                                             dgamma_k.data_ptr(), workspace.data_ptr(), L, H,
+                                             torch.cuda.current_stream(dev).cuda_stream)
+    _raise_on(lib, "h3attn_qk_prologue_backward", st)
+    return dgamma_q, dgamma_k
 
 
 def abi_version() -> int:

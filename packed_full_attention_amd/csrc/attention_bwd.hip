@@ -1,0 +1,446 @@
+// Backward of full bidirectional (non-causal, unmasked) attention for gfx950.
+//
+// Why: the "MiniMax-H3 WS1/WS2 kernel roadmap" RFC, section 7 ("Acceptance
+// gates", per-operator gate) asks for forward and backward of each operator;
+// the operator is its section 5 work item h3_full_attention.
+//
+// Operation, per head, with S = scale Q K^T (Q, K the prologue outputs),
+// P = softmax rows of S, O = P V, and dO the gradient of the output:
+//   dV = P^T dO
+//   dP = dO V^T,  delta_i = sum_d dO_id O_id,  dS = P * (dP - delta)
+//   dQ = scale dS K,  dK = scale dS^T Q
+// P is recomputed from the forward's log-sum-exp: P_ij = 2^(c s_ij - lse_i log2 e),
+// c = scale log2 e, with keys and queries past L excluded.
+//
+// Numerical contract as in the forward: bf16 operands on the matrix cores
+// (P and dS are rounded to bf16 where they become an operand), fp32
+// accumulation, one fixed order over the streamed rows, no atomics and no
+// split: every output row is produced by exactly one wave, so results do not
+// depend on the grid.
+//
+// Three kernels, each a workgroup of 8 waves owning 256 rows of one head
+// (32 per wave) and streaming the other side through LDS in 64-row tiles:
+//   dq:  rows = queries; streams K and V.  Per tile S^T = K Q^T and
+//        dP^T = V dO^T (K, V row operands from LDS; Q^T, dO^T held in
+//        registers), dS^T from them, dQ^T += K^T dS^T (K^T gathered by
+//        transposing LDS reads).  It also computes delta for its rows.
+//   dkv<dV>: rows = keys; streams Q, dO and lse.  Per 32-query block
+//        S = Q K^T (Q from LDS, K^T in registers), P, dV^T += dO^T P.
+//   dkv<dK>: the same with dP = dO V^T, dS, dK^T += Q^T dS (also delta).
+// Computing the transposed product of the side whose rows the wave owns puts
+// one of its rows in each lane column, so the fp32 accumulators of S (or
+// S^T) convert in place to the bf16 B operand of the next product, in the
+// key (query) order that the transposing reads of the streamed tile produce
+// -- the same layout the forward kernel uses for P^T V.  dK and dV are two
+// launches so that each keeps its accumulators, operands and scores within
+// the 256 registers of two waves per SIMD; they recompute S once more.
+//
+// Tiles arrive by buffer_load_dwordx4 ... lds into a ring of three slots
+// (no VGPR staging), one barrier per tile; tiles are row-major with chunk c of
+// row r at c ^ swz(r) (conflict-free row and transposing reads).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "h3attn_internal.h"
+
+namespace h3attn {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
+typedef __attribute__((address_space(3))) const f32x4_t lds_f32x4;
+
+constexpr int kD = 128;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;                       // rows a workgroup owns
+constexpr int kTile = 64;                                // rows per streamed tile
+constexpr int kTileBytes = kTile * kD * 2;               // 16 KiB
+constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;  // 1 KiB pieces per wave per tile
+constexpr int kStages = 3;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBufferDword3 = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t r;
+  r[0] = (__bf16)a;  // round to nearest even
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// ---------------------------------------------------------------- tile DMA
+// A 64-row tile of a [L][H][128] tensor: 16 pieces of 1 KiB, wave w writing
+// pieces w and w + 8; slot (row r, physical chunk p) <- row r, channels
+// 8 (p ^ swz(r)) .. +7.  The buffer resource ends at the tensor's last row,
+// so rows past L read as zeros and no address leaves the tensor.
+struct DmaOffsets {
+  uint32_t off[kDmaPerWave];
+};
+
+__device__ __forceinline__ DmaOffsets dma_offsets(int64_t tok_stride, int wave, int lane) {
+  DmaOffsets d;
+#pragma unroll
+  for (int it = 0; it < kDmaPerWave; ++it) {
+    const int slot = (it * kWaves + wave) * 64 + lane;
+    const int r = slot >> 4;
+    const int c = (slot & 15) ^ swz(r);
+    d.off[it] = (uint32_t)(((int64_t)r * tok_stride + 8 * c) * 2);
+  }
+  return d;
+}
+
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, int64_t valid_bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t n = valid_bytes <= 0 ? 0u : valid_bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)valid_bytes;
+  return i32x4_t{(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
+                 (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)),
+                 (int)__builtin_amdgcn_readfirstlane(n), kBufferDword3};
+}
+
+// 64 lanes x 16 bytes from rsrc + voff (per lane) into LDS at lds (lane order).
+__device__ __forceinline__ void dma_piece(const i32x4_t& rsrc, uint32_t voff, uint32_t lds) {
+  // One wait state between writing M0 and the LDS-DMA instruction that reads it.
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :
+               : "v"(voff), "s"(lds), "s"(rsrc)
+               : "memory");
+}
+
+// Row tile t of the tensor at base (this head's row 0; rows tok_stride
+// elements apart) into LDS at lds_tile: this wave's pieces.
+__device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t tok_stride, int t, int L,
+                                         const DmaOffsets& d, uint32_t lds_tile, int wave) {
+  const int64_t row_bytes = tok_stride * 2;
+  const i32x4_t rsrc = buffer_rsrc(base + (int64_t)t * kTile * tok_stride,
+                                   (int64_t)(L - 1 - t * kTile) * row_bytes + kD * 2);
+#pragma unroll
+  for (int it = 0; it < kDmaPerWave; ++it)
+    dma_piece(rsrc, d.off[it], __builtin_amdgcn_readfirstlane(lds_tile + (it * kWaves + wave) * 1024));
+}
+
+// The 64 fp32 values v[t*64 .. t*64+63] (zeros past L) into LDS at lds (one
+// piece: lanes 16..63 read past the 256 valid bytes and write zeros).
+__device__ __forceinline__ void dma_vec(const float* v, int t, int L, uint32_t lds, int lane) {
+  dma_piece(buffer_rsrc(v + (int64_t)t * kTile, (int64_t)(L - t * kTile) * 4), 16u * lane,
+            __builtin_amdgcn_readfirstlane(lds));
+}
+
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); }
+template <int n>
+__device__ __forceinline__ void dma_wait_all_but() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(n)); }
+
+// ---------------------------------------------------------------- LDS operands
+// Row operand of a tile (32-row block blk, k-step ks): lane reads row
+// 32 blk + col, channels 16 ks + 8 g .. +7 (the A operand whose rows are the
+// tile's rows).  Transposing operand (d-block dblk, 16-row step j): lane
+// receives channel 32 dblk + col of rows 16 j + {4g .. 4g+3, 8+4g .. 11+4g},
+// by two ds_read_b64_tr_b16 -- the row order of a 32x32 accumulator's slots
+// in lane half g, so a packed accumulator is the matching B operand.
+struct Addr {
+  uint32_t row, tr0, tr1;
+};
+
+__device__ __forceinline__ Addr lds_addresses(int lane) {
+  const int col = lane & 31, g = lane >> 5;
+  const int key_a = 4 * g + ((lane & 15) >> 2);             // transposing-read row of this lane
+  const int ch = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // transposing-read channel
+  Addr a;
+  a.row = 256u * col + ((16u * g) ^ (16u * swz(col)));
+  a.tr0 = 256u * key_a + 8u * ((ch >> 2) & 1) + ((16u * (ch >> 3)) ^ (16u * swz(key_a)));
+  a.tr1 = 256u * (8 + key_a) + 8u * ((ch >> 2) & 1) + ((16u * (ch >> 3)) ^ (16u * swz(8 + key_a)));
+  return a;
+}
+
+__device__ __forceinline__ bf16x8_t row_operand(const lds_char* tile, int blk, int ks, const Addr& a) {
+  return *(const lds_bf16x8*)(tile + blk * 8192 + (a.row ^ (32u * ks)));
+}
+
+__device__ __forceinline__ bf16x8_t tr_operand(const lds_char* tile, int dblk, int j, const Addr& a) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + 4096 * j + (a.tr0 ^ (64u * dblk))));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + 4096 * j + (a.tr1 ^ (64u * dblk))));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// The 16 slots of an accumulator, rounded to bf16, as two B operands: slots
+// 0..7 (rows 4g.., 8+4g..) and 8..15 (rows 16+4g.., 24+4g..).
+__device__ __forceinline__ void pack_operands(const float (&x)[16], bf16x8_t (&p)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    p[h] = __builtin_bit_cast(bf16x8_t, u32x4_t{pack_bf16x2(x[8 * h], x[8 * h + 1]),
+                                                pack_bf16x2(x[8 * h + 2], x[8 * h + 3]),
+                                                pack_bf16x2(x[8 * h + 4], x[8 * h + 5]),
+                                                pack_bf16x2(x[8 * h + 6], x[8 * h + 7])});
+}
+
+// One 32-row block of a [L][H][128] tensor as the B operand of a 32x32x16
+// MFMA: lane holds row (row0 + col), channels 16 ks + 8 g .. +7; zeros past L.
+__device__ __forceinline__ void load_row_operands(const uint16_t* base, int64_t tok_stride, int row, int L, int g,
+                                                  bf16x8_t (&op)[8]) {
+  if (row < L) {
+    const uint16_t* p = base + (int64_t)row * tok_stride + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) op[ks] = *reinterpret_cast<const bf16x8_t*>(p + 16 * ks);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) op[ks] = bf16x8_t{};
+  }
+}
+
+// acc[dblk][4 rr + qq] = X^T[32 dblk + 8 rr + 4 g + qq][col] -> x[row][d] * f, bf16.
+__device__ __forceinline__ void store_transposed(uint16_t* row_ptr, const f32x16_t (&acc)[4], float f, int g) {
+#pragma unroll
+  for (int dblk = 0; dblk < 4; ++dblk)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int d = 32 * dblk + 8 * rr + 4 * g;
+      *reinterpret_cast<uint2*>(row_ptr + d) =
+          make_uint2(pack_bf16x2(acc[dblk][4 * rr] * f, acc[dblk][4 * rr + 1] * f),
+                     pack_bf16x2(acc[dblk][4 * rr + 2] * f, acc[dblk][4 * rr + 3] * f));
+    }
+}
+
+// Blocks b < H * n_full take the full 256-row tiles, renumbered so each XCD
+// (block b -> XCD b % 8) gets a contiguous run of them; the last H blocks
+// take each head's partial tile.
+__device__ __forceinline__ void block_tile(int b, int H, int n_full, int& head, int& tile) {
+  const int nfb = H * n_full;
+  if (b < nfb) {
+    const int xcd = b & 7, slot = b >> 3, per = nfb >> 3, rem = nfb & 7;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
+    head = logical / n_full;
+    tile = logical - head * n_full;
+  } else {
+    head = b - nfb;
+    tile = n_full;
+  }
+}
+
+// ---------------------------------------------------------------- dq (+ delta)
+__global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ out, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    uint16_t* __restrict__ dq, float* __restrict__ delta, int L, int H, float c, float scale, int n_full) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStages * kTileBytes];  // K ring, then V ring
+  int head, qtile;
+  block_tile(blockIdx.x, H, n_full, head, qtile);
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tok_stride = (int64_t)H * kD;
+  const int n_tiles = (L + kTile - 1) / kTile;
+  const lds_char* lds = (const lds_char*)lds_raw;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)lds_raw;
+  const DmaOffsets dmo = dma_offsets(tok_stride, wave, lane);
+  const uint16_t* kh = k + (int64_t)head * kD;
+  const uint16_t* vh = v + (int64_t)head * kD;
+  auto fill = [&](int t) {
+    const int tt = t < n_tiles ? t : n_tiles - 1;  // refetch past the end keeps the count fixed
+    const uint32_t s = (uint32_t)(t % kStages) * kTileBytes;
+    dma_rows(kh, tok_stride, tt, L, dmo, lds_base + s, wave);
+    dma_rows(vh, tok_stride, tt, L, dmo, lds_base + kStages * kTileBytes + s, wave);
+  };
+  fill(0);
+  fill(1);
+
+  const int row = qtile * kRows + wave * 32 + col;
+  const bool valid = row < L;
+  bf16x8_t qop[8], dop[8];
+  load_row_operands(q + (int64_t)head * kD, tok_stride, row, L, g, qop);
+  load_row_operands(dout + (int64_t)head * kD, tok_stride, row, L, g, dop);
+  float dsum = 0.f;  // delta = <dO, O> over this lane's 64 channels, then both halves
+  {
+    bf16x8_t oop[8];
+    load_row_operands(out + (int64_t)head * kD, tok_stride, row, L, g, oop);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dsum = fmaf((float)dop[ks][i], (float)oop[ks][i], dsum);
+  }
+  const float dl = pair_sum(dsum);
+  if (valid && g == 0) delta[(int64_t)head * L + row] = dl;
+  const float lse2 = valid ? lse[(int64_t)head * L + row] * kLog2e : 0.f;
+  const Addr a = lds_addresses(lane);
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
+  dma_wait();
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    fill(t + 2);  // into the slot of tile t-1, which every wave finished before the last barrier
+    const lds_char* kt = lds + (t % kStages) * kTileBytes;
+    const lds_char* vt = lds + kStages * kTileBytes + (t % kStages) * kTileBytes;
+    // One 32-key block at a time (keeps two score blocks' registers free).
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        s = mfma32(row_operand(kt, kb, ks, a), qop[ks], s);
+        dp = mfma32(row_operand(vt, kb, ks, a), dop[ks], dp);
+      }
+      // dS^T = P^T (dP^T - delta); slot 4 rr + qq is key 32 kb + 8 rr + 4 g + qq.
+      float x[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = t * kTile + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+        const float p = key < L ? __builtin_amdgcn_exp2f(fmaf(s[e], c, -lse2)) : 0.f;
+        x[e] = p * (dp[e] - dl);
+      }
+      bf16x8_t ds[2];
+      pack_operands(x, ds);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int dblk = 0; dblk < 4; ++dblk)
+          acc[dblk] = mfma32(tr_operand(kt, dblk, 2 * kb + jj, a), ds[jj], acc[dblk]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    dma_wait_all_but<2 * kDmaPerWave>();  // tile t+1 landed (tile t+2 may be in flight)
+    __syncthreads();
+  }
+  dma_wait();
+  if (valid) store_transposed(dq + (int64_t)row * tok_stride + (int64_t)head * kD, acc, scale, g);
+}
+
+// ---------------------------------------------------------------- dk, dv
+// Ring slot: Q tile, dO tile, then 1 KiB of lse and (dK) 1 KiB of delta.
+constexpr int kSlotBytes = 2 * kTileBytes + 2048;
+
+template <bool kDK>
+__global__ __launch_bounds__(kThreads, 1) void attention_bwd_dkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    uint16_t* __restrict__ res, int L, int H, float c, float scale, int n_full) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kStages * kSlotBytes];
+  int head, ktile;
+  block_tile(blockIdx.x, H, n_full, head, ktile);
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tok_stride = (int64_t)H * kD;
+  const int n_tiles = (L + kTile - 1) / kTile;
+  const lds_char* lds = (const lds_char*)lds_raw;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)lds_raw;
+  const DmaOffsets dmo = dma_offsets(tok_stride, wave, lane);
+  const uint16_t* qh = q + (int64_t)head * kD;
+  const uint16_t* doh = dout + (int64_t)head * kD;
+  const float* lseh = lse + (int64_t)head * L;
+  const float* dlh = delta + (int64_t)head * L;
+  auto fill = [&](int t) {
+    const int tt = t < n_tiles ? t : n_tiles - 1;
+    const uint32_t s = lds_base + (uint32_t)(t % kStages) * kSlotBytes;
+    dma_rows(qh, tok_stride, tt, L, dmo, s, wave);
+    dma_rows(doh, tok_stride, tt, L, dmo, s + kTileBytes, wave);
+    if (wave == 0) dma_vec(lseh, tt, L, s + 2 * kTileBytes, lane);
+    if (kDK && wave == 1) dma_vec(dlh, tt, L, s + 2 * kTileBytes + 1024, lane);
+  };
+  // Waves that issue a vector piece have one more DMA per tile in flight.
+  auto wait_all_but_last_tile = [&]() {
+    if (wave == 0 || (kDK && wave == 1)) dma_wait_all_but<2 * kDmaPerWave + 1>();
+    else dma_wait_all_but<2 * kDmaPerWave>();
+  };
+  fill(0);
+  fill(1);
+
+  const int key = ktile * kRows + wave * 32 + col;
+  bf16x8_t kop[8], vop[8];
+  load_row_operands(k + (int64_t)head * kD, tok_stride, key, L, g, kop);
+  if (kDK) load_row_operands(v + (int64_t)head * kD, tok_stride, key, L, g, vop);
+  const Addr a = lds_addresses(lane);
+  f32x16_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
+  dma_wait();
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    fill(t + 2);
+    const lds_char* slot = lds + (t % kStages) * kSlotBytes;
+    const lds_char* qt = slot;
+    const lds_char* dot = slot + kTileBytes;
+    const lds_char* vec = slot + 2 * kTileBytes;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // S = Q K^T (32 queries x this wave's 32 keys); slot 4 rr + qq is query
+      // 32 qb + 8 rr + 4 g + qq of the tile.
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        s = mfma32(row_operand(qt, qb, ks, a), kop[ks], s);
+        if (kDK) dp = mfma32(row_operand(dot, qb, ks, a), vop[ks], dp);
+      }
+      float x[16];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r0 = 32 * qb + 8 * rr + 4 * g;
+        const f32x4_t l4 = *(const lds_f32x4*)(vec + 4 * r0);
+        f32x4_t d4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (kDK) d4 = *(const lds_f32x4*)(vec + 1024 + 4 * r0);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int e = 4 * rr + qq;
+          const float p = t * kTile + r0 + qq < L ? __builtin_amdgcn_exp2f(fmaf(s[e], c, -l4[qq] * kLog2e)) : 0.f;
+          x[e] = kDK ? p * (dp[e] - d4[qq]) : p;
+        }
+      }
+      bf16x8_t w[2];
+      pack_operands(x, w);
+      // dV^T += dO^T P, or dK^T += Q^T dS: A gathered from the tile by
+      // transposing reads in the accumulator's query order.
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int dblk = 0; dblk < 4; ++dblk)
+          acc[dblk] = mfma32(tr_operand(kDK ? qt : dot, dblk, 2 * qb + jj, a), w[jj], acc[dblk]);
+    }
+    wait_all_but_last_tile();  // tile t+1 landed (tile t+2 may be in flight)
+    __syncthreads();
+  }
+  dma_wait();
+  if (key < L) store_transposed(res + (int64_t)key * tok_stride + (int64_t)head * kD, acc, kDK ? scale : 1.0f, g);
+}
+
+}  // namespace
+
+int64_t backward_grid_blocks(int64_t L, int32_t H) { return ((L + kRows - 1) / kRows) * (int64_t)H; }
+int backward_block_threads() { return kThreads; }
+
+hipError_t launch_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* out, const uint16_t* dout, const float* lse,
+                                     uint16_t* dq, uint16_t* dk, uint16_t* dv, float* delta, int64_t L,
+                                     int32_t H, float scale, hipStream_t stream) {
+  const dim3 grid((unsigned)backward_grid_blocks(L, H)), block(kThreads);
+  const int n_full = (int)(L / kRows);
+  const float c = scale * kLog2e;
+  hipLaunchKernelGGL(attention_bwd_dq_kernel, grid, block, 0, stream, q, k, v, out, dout, lse, dq, delta, (int)L,
+                     (int)H, c, scale, n_full);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attention_bwd_dkv_kernel<false>, grid, block, 0, stream, q, k, v, dout, lse, delta, dv,
+                     (int)L, (int)H, c, scale, n_full);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attention_bwd_dkv_kernel<true>, grid, block, 0, stream, q, k, v, dout, lse, delta, dk,
+                     (int)L, (int)H, c, scale, n_full);
+  return hipGetLastError();
+}
+
+}  // namespace h3attn

@@ -112,6 +112,7 @@ constexpr int kTileBytes = kBN * kD * 2;  // 16 KiB per K or V tile
 constexpr int kStages = 4;                // tiles per ring (resident or in flight)
 constexpr int kVRing = kStages * kTileBytes;  // the V ring follows the K ring
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSumBound = 256.0f;        // a lane's tile sum of P above this moves the offset
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -565,7 +566,7 @@ __device__ __forceinline__ void stream_only(const Ctx& x) {
 template <bool kLog2, bool kVT>
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, int L, int H, int Lp, float scale_log2e, int n_qfull) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int L, int H, int Lp, float scale_log2e, int n_qfull) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStages * kTileBytes];
 
   // Blocks are dispatched in increasing order, round-robin over the 8 XCDs
@@ -707,8 +708,13 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   }
   dma_wait();  // the refetches past the end, before the workgroup exits
 
-  // Epilogue: full row sum = both lane-halves; O / l -> bf16.
-  const float inv_l = 1.0f / pair_sum(st.l);
+  // Epilogue: full row sum = both lane-halves; O / l -> bf16.  With lse, the
+  // row's natural log-sum-exp of the scaled scores, ln 2 * log2(sum_j 2^(c s_j))
+  // = ln 2 * (c m + log2 l) (log2 variant: m + log2 l), for the backward pass.
+  const float l_row = pair_sum(st.l);
+  const float inv_l = 1.0f / l_row;
+  if (lse != nullptr && x.g == 0 && qrow < L)
+    lse[(int64_t)head * L + qrow] = kLn2 * ((kLog2 ? st.m : st.m * x.c) + log2f(l_row));
   if (qrow < L) {
     uint16_t* po = out + (int64_t)qrow * tok_stride + (int64_t)head * kD;
 #pragma unroll
@@ -782,15 +788,15 @@ hipError_t launch_v_transpose(const uint16_t* v, uint16_t* vt, int64_t L, int32_
 }
 
 hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                    uint16_t* out, int64_t L, int32_t H, float scale, bool log2,
+                                    uint16_t* out, float* lse, int64_t L, int32_t H, float scale, bool log2,
                                     hipStream_t stream) {
   const int n_qfull = (int)(L / kBM);  // full 256-row q-tiles per head
   const dim3 grid((unsigned)attention_grid_blocks(L, H));
   if (log2)  // v is V^T
-    hipLaunchKernelGGL((attention_fwd_kernel<true, true>), grid, dim3(kThreads), 0, stream, q, k, v, out,
+    hipLaunchKernelGGL((attention_fwd_kernel<true, true>), grid, dim3(kThreads), 0, stream, q, k, v, out, lse,
                        (int)L, (int)H, (int)vt_padded_length(L), 1.0f, n_qfull);
   else
-    hipLaunchKernelGGL((attention_fwd_kernel<false, false>), grid, dim3(kThreads), 0, stream, q, k, v, out,
+    hipLaunchKernelGGL((attention_fwd_kernel<false, false>), grid, dim3(kThreads), 0, stream, q, k, v, out, lse,
                        (int)L, (int)H, 0, scale * kLog2e, n_qfull);
   return hipGetLastError();
 }

@@ -87,7 +87,7 @@ int prologue(void* q, void* k, const float* gamma_q, const float* gamma_k, const
 }
 
 int forward(const void* q, const void* k, const void* v, void* out, int64_t L, int32_t H, float scale,
-            bool log2, hipStream_t stream) {
+            bool log2, hipStream_t stream, float* lse = nullptr) {
   if (!q || !k || !v || !out) return fail(H3A_EINVAL, "null pointer argument%s");
   uint64_t bytes = 0;
   if (int s = check_shape(L, H, &bytes)) return s;
@@ -98,11 +98,18 @@ int forward(const void* q, const void* k, const void* v, void* out, int64_t L, i
   const uint64_t vbytes = log2 ? (uint64_t)h3attn::vt_bytes(L, H) : bytes;
   if (overlap(out, bytes, q, bytes) || overlap(out, bytes, k, bytes) || overlap(out, bytes, v, vbytes))
     return fail(H3A_EINVAL, log2 ? "out overlaps q, k or vt%s" : "out overlaps q, k or v%s");
+  if (lse != nullptr) {
+    const uint64_t lbytes = (uint64_t)L * H * 4;
+    if (!aligned(lse, 4)) return fail(H3A_EINVAL, "lse must be 4-byte aligned%s");
+    if (overlap(lse, lbytes, q, bytes) || overlap(lse, lbytes, k, bytes) || overlap(lse, lbytes, v, vbytes) ||
+        overlap(lse, lbytes, out, bytes))
+      return fail(H3A_EINVAL, "lse overlaps q, k, v or out%s");
+  }
   if (h3attn::attention_grid_blocks(L, H) * h3attn::attention_block_threads() >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "attention grid too large for (L, H)%s");
   const hipError_t e = h3attn::launch_attention_forward(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-      static_cast<uint16_t*>(out), L, H, scale, log2, stream);
+      static_cast<uint16_t*>(out), lse, L, H, scale, log2, stream);
   if (e != hipSuccess) return fail(H3A_EHIP, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -148,6 +155,94 @@ int h3attn_forward(const void* q, const void* k, const void* v, void* out, int64
 int h3attn_forward_log2(const void* q, const void* k, const void* vt, void* out, int64_t L, int32_t H,
                         hipStream_t stream) {
   return forward(q, k, vt, out, L, H, 1.0f, true, stream);
+}
+
+int h3attn_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse, int64_t L,
+                       int32_t H, float scale, hipStream_t stream) {
+  if (!lse) return fail(H3A_EINVAL, "null pointer argument%s");
+  return forward(q, k, v, out, L, H, scale, false, stream, lse);
+}
+
+int64_t h3attn_attention_backward_workspace_bytes(int64_t L, int32_t H) {
+  uint64_t bytes = 0;
+  if (check_shape(L, H, &bytes) != H3A_OK) return -1;
+  ok();
+  return L * (int64_t)H * 4;
+}
+
+int h3attn_attention_backward(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              void* workspace, int64_t L, int32_t H, float scale, hipStream_t stream) {
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return fail(H3A_EINVAL, "null pointer argument%s");
+  uint64_t bytes = 0;
+  if (int s = check_shape(L, H, &bytes)) return s;
+  const void* bf[8] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* p : bf)
+    if (!aligned(p, 16)) return fail(H3A_EINVAL, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned%s");
+  if (!aligned(lse, 4) || !aligned(workspace, 4)) return fail(H3A_EINVAL, "lse and workspace must be 4-byte aligned%s");
+  if (!(isfinite(scale) && scale > 0.0f)) return fail(H3A_EINVAL, "scale must be finite and > 0%s");
+  const uint64_t vec = (uint64_t)L * H * 4;
+  // Written ranges: dq, dk, dv, workspace; none may meet another or any input.
+  const void* wr[4] = {dq, dk, dv, workspace};
+  const uint64_t wn[4] = {bytes, bytes, bytes, vec};
+  const void* in[6] = {q, k, v, out, dout, lse};
+  const uint64_t inn[6] = {bytes, bytes, bytes, bytes, bytes, vec};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(wr[i], wn[i], in[j], inn[j])) return fail(H3A_EINVAL, "an output or the workspace overlaps an input%s");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(wr[i], wn[i], wr[j], wn[j])) return fail(H3A_EINVAL, "outputs or workspace overlap%s");
+  }
+  if (h3attn::backward_grid_blocks(L, H) * h3attn::backward_block_threads() >= kMaxThreadsPerGrid)
+    return fail(H3A_EUNSUPPORTED, "backward grid too large for (L, H)%s");
+  const hipError_t e = h3attn::launch_attention_backward(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, static_cast<uint16_t*>(dq),
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), static_cast<float*>(workspace), L, H, scale, stream);
+  if (e != hipSuccess) return fail(H3A_EHIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int64_t h3attn_qk_prologue_backward_workspace_bytes(int64_t L, int32_t H) {
+  uint64_t bytes = 0;
+  if (check_shape(L, H, &bytes) != H3A_OK) return -1;
+  ok();
+  return h3attn::prologue_backward_workspace_bytes(L);
+}
+
+int h3attn_qk_prologue_backward(const void* q, const void* k, const float* gamma_q, const float* gamma_k,
+                                const int32_t* pos_thw, void* dq, void* dk, float* dgamma_q,
+                                float* dgamma_k, void* workspace, int64_t L, int32_t H,
+                                hipStream_t stream) {
+  if (!q || !k || !gamma_q || !gamma_k || !pos_thw || !dq || !dk || !dgamma_q || !dgamma_k || !workspace)
+    return fail(H3A_EINVAL, "null pointer argument%s");
+  uint64_t bytes = 0;
+  if (int s = check_shape(L, H, &bytes)) return s;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(dq, 16) || !aligned(dk, 16))
+    return fail(H3A_EINVAL, "q, k, dq and dk must be 16-byte aligned%s");
+  if (!aligned(gamma_q, 4) || !aligned(gamma_k, 4) || !aligned(pos_thw, 4) || !aligned(dgamma_q, 4) ||
+      !aligned(dgamma_k, 4) || !aligned(workspace, 4))
+    return fail(H3A_EINVAL, "gammas, positions, gamma gradients and workspace must be 4-byte aligned%s");
+  const uint64_t ws = (uint64_t)h3attn::prologue_backward_workspace_bytes(L);
+  const void* wr[5] = {dq, dk, dgamma_q, dgamma_k, workspace};
+  const uint64_t wn[5] = {bytes, bytes, 512, 512, ws};
+  const void* in[5] = {q, k, gamma_q, gamma_k, pos_thw};
+  const uint64_t inn[5] = {bytes, bytes, 512, 512, (uint64_t)L * 12};
+  for (int i = 0; i < 5; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlap(wr[i], wn[i], in[j], inn[j])) return fail(H3A_EINVAL, "an output or the workspace overlaps an input%s");
+    for (int j = i + 1; j < 5; ++j)
+      if (overlap(wr[i], wn[i], wr[j], wn[j])) return fail(H3A_EINVAL, "outputs or workspace overlap%s");
+  }
+  if (h3attn::prologue_grid_blocks(L) * 256 >= kMaxThreadsPerGrid)
+    return fail(H3A_EUNSUPPORTED, "prologue grid too large for L%s");
+  const hipError_t e = h3attn::launch_qk_prologue_backward(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), gamma_q, gamma_k, pos_thw,
+      static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), dgamma_q, dgamma_k, static_cast<float*>(workspace), L,
+      H, stream);
+  if (e != hipSuccess) return fail(H3A_EHIP, "prologue backward launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 }  // extern "C"

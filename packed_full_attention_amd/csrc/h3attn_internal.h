@@ -16,10 +16,29 @@ hipError_t launch_qk_prologue(uint16_t* q, uint16_t* k, const float* gamma_q,
 // Enqueue the flash-attention forward kernel.  log2 = false: weights
 // exp(scale <q,k>), v row-major [L][H][128]; log2 = true: weights 2^<q,k>
 // (q already carries the softmax scale times log2(e)), scale ignored, and v
-// is V^T as written by launch_v_transpose.
+// is V^T as written by launch_v_transpose.  lse (may be null): fp32 [H][L],
+// each row's natural log-sum-exp of its scaled scores.
 hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                    uint16_t* out, int64_t L, int32_t H, float scale, bool log2,
+                                    uint16_t* out, float* lse, int64_t L, int32_t H, float scale, bool log2,
                                     hipStream_t stream);
+
+// Enqueue the attention backward (three kernels, in this order): dq and the
+// per-row delta = <dout, out> (fp32 [H][L], written), then dv, then dk.
+// q, k are the prologue outputs, lse the forward's [H][L] log-sum-exp.
+hipError_t launch_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* out, const uint16_t* dout, const float* lse,
+                                     uint16_t* dq, uint16_t* dk, uint16_t* dv, float* delta, int64_t L,
+                                     int32_t H, float scale, hipStream_t stream);
+int64_t backward_grid_blocks(int64_t L, int32_t H);
+int backward_block_threads();
+
+// Backward of the prologue (in place on dq, dk) and the gamma gradients;
+// workspace of prologue_backward_workspace_bytes(L) bytes.
+hipError_t launch_qk_prologue_backward(const uint16_t* q, const uint16_t* k, const float* gamma_q,
+                                       const float* gamma_k, const int32_t* pos, uint16_t* dq, uint16_t* dk,
+                                       float* dgamma_q, float* dgamma_k, float* workspace, int64_t L, int32_t H,
+                                       hipStream_t stream);
+int64_t prologue_backward_workspace_bytes(int64_t L);
 
 // V^T = [H][128][Lp] bf16, Lp = L rounded up to 64, zeros past L.
 hipError_t launch_v_transpose(const uint16_t* v, uint16_t* vt, int64_t L, int32_t H, hipStream_t stream);

@@ -134,6 +134,164 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
   }
 }
 
+// ---------------------------------------------------------------- backward
+// Gradient of the prologue (same RFC, section 7, per-operator gate: forward
+// and backward), for every row of Q and of K, given dy' = dLoss/d(output):
+//   dy = inverse rotation of dy': for c < 48, dy_c = cos dy'_c + sin dy'_{c+48},
+//        dy_{c+48} = cos dy'_{c+48} - sin dy'_c; dy_c = dy'_c for c >= 96
+//   dx = r (gamma dy) - x r^3 mean(gamma dy x),  r = (mean(x^2) + eps)^(-1/2)
+//   dgamma += dy x r   (summed over every token and head)
+// x is the raw (pre-prologue) row; dx overwrites dy' in place (bf16, one RNE
+// rounding).  Same mapping as the forward (one wave per token, a 16-lane
+// quarter-wave per row, each rotation pair inside one lane).  The gamma
+// gradients are summed without atomics: each lane keeps its channels' sums
+// over the rows it handles, the workgroup adds its four waves in LDS in a
+// fixed order and writes one partial per workgroup, and gamma_reduce_kernel
+// adds those partials in a fixed order -- the result does not depend on timing.
+__global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_bwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ gamma_q,
+    const float* __restrict__ gamma_k, const int32_t* __restrict__ pos, uint16_t* __restrict__ dq,
+    uint16_t* __restrict__ dk, float* __restrict__ partial, int64_t L, int32_t H) {
+  __shared__ float wsum[kWavesPerBlock][2 * kHeadDim];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t token = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  const bool live = token < L;
+  const int sub = lane >> 4, i = lane & 15;
+  const bool pair_lane = i < 12;
+  const int ch_a = pair_lane ? 4 * i : 96 + 4 * (i - 12);
+  const int ch_b = pair_lane ? 48 + 4 * i : 112 + 4 * (i - 12);
+  float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
+  if (live && pair_lane) {
+    const float p = (float)pos[token * 3 + (i >> 2)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * (i & 3) + e;
+      const float inv_freq = 1.0f / powf(10000.0f, (float)(2 * j) / 32.0f);
+      sincosf(p * inv_freq, &sn[e], &cs[e]);
+    }
+  }
+  float gqa[4], gqb[4], gka[4], gkb[4];  // gammas at the lane's channels
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    gqa[e] = gamma_q[ch_a + e];
+    gqb[e] = gamma_q[ch_b + e];
+    gka[e] = gamma_k[ch_a + e];
+    gkb[e] = gamma_k[ch_b + e];
+  }
+  float sqa[4] = {}, sqb[4] = {}, ska[4] = {}, skb[4] = {};  // this lane's dgamma sums
+  const int64_t token_base = token * (int64_t)H * kHeadDim;
+  const int rows = live ? 2 * H : 0;
+  const int rows_round = (rows + 3) & ~3;  // every row group runs the same number of passes
+  for (int rr = sub; rr < rows_round; rr += 4) {
+    const bool on = rr < rows;  // all 16 lanes of a row group share rr
+    const int t = rr < H ? 0 : 1;
+    const int64_t off = token_base + (int64_t)(t == 0 ? rr : rr - H) * kHeadDim;
+    uint2 xa = make_uint2(0u, 0u), xb = xa, da = xa, db = xa;
+    if (on) {
+      const uint16_t* xr = (t == 0 ? q : k) + off;
+      const uint16_t* dr = (t == 0 ? dq : dk) + off;
+      xa = *reinterpret_cast<const uint2*>(xr + ch_a);
+      xb = *reinterpret_cast<const uint2*>(xr + ch_b);
+      da = *reinterpret_cast<const uint2*>(dr + ch_a);
+      db = *reinterpret_cast<const uint2*>(dr + ch_b);
+    }
+    const float x_a[4] = {lo_bf16(xa.x), hi_bf16(xa.x), lo_bf16(xa.y), hi_bf16(xa.y)};
+    const float x_b[4] = {lo_bf16(xb.x), hi_bf16(xb.x), lo_bf16(xb.y), hi_bf16(xb.y)};
+    const float d_a[4] = {lo_bf16(da.x), hi_bf16(da.x), lo_bf16(da.y), hi_bf16(da.y)};
+    const float d_b[4] = {lo_bf16(db.x), hi_bf16(db.x), lo_bf16(db.y), hi_bf16(db.y)};
+    float ss = 0.f, tdot = 0.f, ya[4], yb[4], g_a[4], g_b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ss = fmaf(x_a[e], x_a[e], ss);
+      ss = fmaf(x_b[e], x_b[e], ss);
+      ya[e] = fmaf(d_a[e], cs[e], d_b[e] * sn[e]);   // dy at ch_a (pass-through lanes: cs = 1, sn = 0)
+      yb[e] = fmaf(d_b[e], cs[e], -(d_a[e] * sn[e])); // dy at ch_b
+      g_a[e] = (t == 0 ? gqa[e] : gka[e]) * ya[e];
+      g_b[e] = (t == 0 ? gqb[e] : gkb[e]) * yb[e];
+      tdot = fmaf(g_a[e], x_a[e], tdot);
+      tdot = fmaf(g_b[e], x_b[e], tdot);
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      ss += __shfl_xor(ss, m, 16);
+      tdot += __shfl_xor(tdot, m, 16);
+    }
+    const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + 1e-5f);
+    const float corr = r * r * r * tdot * (1.0f / kHeadDim);
+    float oa[4], ob[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      oa[e] = fmaf(r, g_a[e], -(x_a[e] * corr));
+      ob[e] = fmaf(r, g_b[e], -(x_b[e] * corr));
+      const float ua = on ? ya[e] * x_a[e] * r : 0.f, ub = on ? yb[e] * x_b[e] * r : 0.f;
+      if (t == 0) {
+        sqa[e] += ua;
+        sqb[e] += ub;
+      } else {
+        ska[e] += ua;
+        skb[e] += ub;
+      }
+    }
+    if (on) {
+      uint16_t* dr = (t == 0 ? dq : dk) + off;
+      *reinterpret_cast<uint2*>(dr + ch_a) = make_uint2(pack_bf16x2(oa[0], oa[1]), pack_bf16x2(oa[2], oa[3]));
+      *reinterpret_cast<uint2*>(dr + ch_b) = make_uint2(pack_bf16x2(ob[0], ob[1]), pack_bf16x2(ob[2], ob[3]));
+    }
+  }
+  // The four row groups of the wave (lanes i, i+16, i+32, i+48), then the
+  // workgroup's waves in order.
+  auto group_sum = [](float x) {
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+  };
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sqa[e] = group_sum(sqa[e]);
+    sqb[e] = group_sum(sqb[e]);
+    ska[e] = group_sum(ska[e]);
+    skb[e] = group_sum(skb[e]);
+  }
+  if (sub == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wsum[wave][ch_a + e] = sqa[e];
+      wsum[wave][ch_b + e] = sqb[e];
+      wsum[wave][kHeadDim + ch_a + e] = ska[e];
+      wsum[wave][kHeadDim + ch_b + e] = skb[e];
+    }
+  }
+  __syncthreads();
+  const int c = threadIdx.x;  // 256 threads = 2 x 128 channels
+  float acc = wsum[0][c];
+#pragma unroll
+  for (int w = 1; w < kWavesPerBlock; ++w) acc += wsum[w][c];
+  partial[(int64_t)blockIdx.x * 2 * kHeadDim + c] = acc;
+}
+
+// out[j][c] = sum over rows j*256 .. j*256+255 (< n) of in[row][c], c < 256,
+// rows added in increasing order.
+constexpr int kReduceRows = 256;
+
+__global__ __launch_bounds__(2 * kHeadDim) void gamma_reduce_kernel(const float* __restrict__ in,
+                                                                    float* __restrict__ out, int64_t n) {
+  const int c = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * kReduceRows;
+  const int64_t r1 = r0 + kReduceRows < n ? r0 + kReduceRows : n;
+  float acc = 0.f;
+  for (int64_t r = r0; r < r1; ++r) acc += in[r * 2 * kHeadDim + c];
+  out[(int64_t)blockIdx.x * 2 * kHeadDim + c] = acc;
+}
+
+// The last stage: 256 sums -> dgamma_q (c < 128), dgamma_k.
+__global__ __launch_bounds__(2 * kHeadDim) void gamma_final_kernel(const float* __restrict__ in, float* __restrict__ dgq,
+                                                                   float* __restrict__ dgk, int64_t n) {
+  const int c = threadIdx.x;
+  float acc = 0.f;
+  for (int64_t r = 0; r < n; ++r) acc += in[r * 2 * kHeadDim + c];
+  if (c < kHeadDim) dgq[c] = acc;
+  else dgk[c - kHeadDim] = acc;
+}
+
 }  // namespace
 
 int64_t prologue_grid_blocks(int64_t L) { return (L + kWavesPerBlock - 1) / kWavesPerBlock; }
@@ -165,6 +323,33 @@ hipError_t launch_qk_prologue(uint16_t* q, uint16_t* k, const float* gamma_q, co
       hipLaunchKernelGGL(qk_prologue_kernel<4>, grid, block, 0, stream, q, k, gamma_q, gamma_k, pos, L, H, q_scale);
       break;
   }
+  return hipGetLastError();
+}
+
+// Workspace of the backward: one 256-float partial per workgroup, then one per
+// 256 of those.
+static int64_t bwd_blocks(int64_t L) { return prologue_grid_blocks(L); }
+static int64_t bwd_groups(int64_t L) { return (bwd_blocks(L) + kReduceRows - 1) / kReduceRows; }
+
+int64_t prologue_backward_workspace_bytes(int64_t L) {
+  return (bwd_blocks(L) + bwd_groups(L)) * 2 * kHeadDim * (int64_t)sizeof(float);
+}
+
+hipError_t launch_qk_prologue_backward(const uint16_t* q, const uint16_t* k, const float* gamma_q,
+                                       const float* gamma_k, const int32_t* pos, uint16_t* dq, uint16_t* dk,
+                                       float* dgamma_q, float* dgamma_k, float* workspace, int64_t L, int32_t H,
+                                       hipStream_t stream) {
+  const int64_t nb = bwd_blocks(L), ng = bwd_groups(L);
+  float* partial = workspace;
+  float* groups = workspace + nb * 2 * kHeadDim;
+  hipLaunchKernelGGL(qk_prologue_bwd_kernel, dim3((unsigned)nb), dim3(kWavesPerBlock * 64), 0, stream, q, k,
+                     gamma_q, gamma_k, pos, dq, dk, partial, L, H);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gamma_reduce_kernel, dim3((unsigned)ng), dim3(2 * kHeadDim), 0, stream, partial, groups, nb);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gamma_final_kernel, dim3(1), dim3(2 * kHeadDim), 0, stream, groups, dgamma_q, dgamma_k, ng);
   return hipGetLastError();
 }
 
