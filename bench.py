@@ -133,7 +133,8 @@ def main() -> int:
 
     import numpy as np
     import torch
-    from packed_full_attention_amd import (h3attn_forward, h3attn_forward_log2, h3attn_qk_prologue,
+    from packed_full_attention_amd import (h3attn_attention_backward, h3attn_forward, h3attn_forward_log2,
+                                           h3attn_forward_lse, h3attn_qk_prologue, h3attn_qk_prologue_backward,
                                            h3attn_qk_prologue_scaled, h3attn_v_transpose, load_library)
     from packed_full_attention_amd import workloads as wl
 
@@ -214,6 +215,30 @@ def main() -> int:
             f(i)
     ms_step, (t_pro, t_vt, t_att), wall_ms = timed(fast, K, W)
     del qs, ks
+
+    # Training pieces, timed separately (not part of `value`): the forward with
+    # log-sum-exp, the attention backward and the prologue backward, on the
+    # prologue's outputs of this workload and a seeded dO.
+    qp, kp = q.clone(), k.clone()
+    h3attn_qk_prologue(qp, kp, gq, gk, pos)
+    gen = torch.Generator(device=dev).manual_seed(1000 + w.index)
+    dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    out2, lse = torch.empty_like(q), torch.empty(H, L, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(L * H * 4, dtype=torch.uint8, device=dev)
+    pws = torch.empty(int(load_library().h3attn_qk_prologue_backward_workspace_bytes(L, H)), dtype=torch.uint8,
+                      device=dev)
+    dgq, dgk = torch.empty(128, device=dev), torch.empty(128, device=dev)
+    train = [lambda i: h3attn_forward_lse(qp, kp, v, out2, lse, scale=scale),
+             lambda i: h3attn_attention_backward(qp, kp, v, out2, dout, lse, dq, dk, dv, ws, scale=scale),
+             lambda i: h3attn_qk_prologue_backward(q, k, gq, gk, pos, dq, dk, dgq, dgk, pws)]
+    for i in range(W):
+        for f in train:
+            f(i)
+    _, (t_fl, t_bwd, t_pbwd), _ = timed(train, K, W)
+    bwd_flops = 2.5 * attention_flops(L, H)  # dV, dP, dQ, dK and the recomputed S: 5 products of 2 L^2 128
+    pbwd_bytes = 12.0 * L * H * 128 + 12.0 * L + 1024.0  # read q, k, dq', dk'; write dq, dk
+    del qp, kp, dout, out2, lse, dq, dk, dv, ws, pws
     if not bool(torch.isfinite(out.float()).all()):
         print("bench.py: non-finite attention output", file=sys.stderr)
         return 1
@@ -268,6 +293,13 @@ def main() -> int:
                        "attention_ms": round(plain_att, 4),
                        "attention_tflops": round(flops / (plain_att * 1e-3) / 1e12, 2),
                        "prologue_us": round(plain_pro * 1e3, 2)},
+        "backward": {"forward_lse_ms": round(t_fl, 4),
+                     "attention_backward_ms": round(t_bwd, 4),
+                     "attention_backward_tflops": round(bwd_flops / (t_bwd * 1e-3) / 1e12, 2),
+                     "attention_backward_frac": round(bwd_flops / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "flop_count": "2.5 x forward (dV, dP, dQ, dK, S)",
+                     "prologue_backward_us": round(t_pbwd * 1e3, 2),
+                     "prologue_backward_gbs": round(pbwd_bytes / (t_pbwd * 1e-3) / 1e9, 1)},
         "wall_ms_timed_region": round(wall_ms, 2),
     }
     if not args.no_cpu_baseline:

@@ -181,61 +181,76 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_bwd_kernel(
   float sqa[4] = {}, sqb[4] = {}, ska[4] = {}, skb[4] = {};  // this lane's dgamma sums
   const int64_t token_base = token * (int64_t)H * kHeadDim;
   const int rows = live ? 2 * H : 0;
-  const int rows_round = (rows + 3) & ~3;  // every row group runs the same number of passes
-  for (int rr = sub; rr < rows_round; rr += 4) {
-    const bool on = rr < rows;  // all 16 lanes of a row group share rr
-    const int t = rr < H ? 0 : 1;
-    const int64_t off = token_base + (int64_t)(t == 0 ? rr : rr - H) * kHeadDim;
-    uint2 xa = make_uint2(0u, 0u), xb = xa, da = xa, db = xa;
-    if (on) {
-      const uint16_t* xr = (t == 0 ? q : k) + off;
-      const uint16_t* dr = (t == 0 ? dq : dk) + off;
-      xa = *reinterpret_cast<const uint2*>(xr + ch_a);
-      xb = *reinterpret_cast<const uint2*>(xr + ch_b);
-      da = *reinterpret_cast<const uint2*>(dr + ch_a);
-      db = *reinterpret_cast<const uint2*>(dr + ch_b);
-    }
-    const float x_a[4] = {lo_bf16(xa.x), hi_bf16(xa.x), lo_bf16(xa.y), hi_bf16(xa.y)};
-    const float x_b[4] = {lo_bf16(xb.x), hi_bf16(xb.x), lo_bf16(xb.y), hi_bf16(xb.y)};
-    const float d_a[4] = {lo_bf16(da.x), hi_bf16(da.x), lo_bf16(da.y), hi_bf16(da.y)};
-    const float d_b[4] = {lo_bf16(db.x), hi_bf16(db.x), lo_bf16(db.y), hi_bf16(db.y)};
-    float ss = 0.f, tdot = 0.f, ya[4], yb[4], g_a[4], g_b[4];
+  // kBwdRows rows per row group per pass, all loaded before any is computed (the
+  // stores go to the buffers the next rows are read from, so the compiler would
+  // not move those loads ahead of them); every row group runs the same passes.
+  constexpr int kBwdRows = 4;
+  const int rows_round = (rows + 4 * kBwdRows - 1) / (4 * kBwdRows) * (4 * kBwdRows);
+  for (int base = 0; base < rows_round; base += 4 * kBwdRows) {
+    uint2 xa[kBwdRows], xb[kBwdRows], da[kBwdRows], db[kBwdRows];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ss = fmaf(x_a[e], x_a[e], ss);
-      ss = fmaf(x_b[e], x_b[e], ss);
-      ya[e] = fmaf(d_a[e], cs[e], d_b[e] * sn[e]);   // dy at ch_a (pass-through lanes: cs = 1, sn = 0)
-      yb[e] = fmaf(d_b[e], cs[e], -(d_a[e] * sn[e])); // dy at ch_b
-      g_a[e] = (t == 0 ? gqa[e] : gka[e]) * ya[e];
-      g_b[e] = (t == 0 ? gqb[e] : gkb[e]) * yb[e];
-      tdot = fmaf(g_a[e], x_a[e], tdot);
-      tdot = fmaf(g_b[e], x_b[e], tdot);
-    }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      ss += __shfl_xor(ss, m, 16);
-      tdot += __shfl_xor(tdot, m, 16);
-    }
-    const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + 1e-5f);
-    const float corr = r * r * r * tdot * (1.0f / kHeadDim);
-    float oa[4], ob[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      oa[e] = fmaf(r, g_a[e], -(x_a[e] * corr));
-      ob[e] = fmaf(r, g_b[e], -(x_b[e] * corr));
-      const float ua = on ? ya[e] * x_a[e] * r : 0.f, ub = on ? yb[e] * x_b[e] * r : 0.f;
-      if (t == 0) {
-        sqa[e] += ua;
-        sqb[e] += ub;
-      } else {
-        ska[e] += ua;
-        skb[e] += ub;
+    for (int n = 0; n < kBwdRows; ++n) {
+      const int rr = base + 4 * n + sub;
+      xa[n] = xb[n] = da[n] = db[n] = make_uint2(0u, 0u);
+      if (rr < rows) {
+        const int t = rr < H ? 0 : 1;
+        const int64_t off = token_base + (int64_t)(t == 0 ? rr : rr - H) * kHeadDim;
+        const uint16_t* xr = (t == 0 ? q : k) + off;
+        const uint16_t* dr = (t == 0 ? dq : dk) + off;
+        xa[n] = *reinterpret_cast<const uint2*>(xr + ch_a);
+        xb[n] = *reinterpret_cast<const uint2*>(xr + ch_b);
+        da[n] = *reinterpret_cast<const uint2*>(dr + ch_a);
+        db[n] = *reinterpret_cast<const uint2*>(dr + ch_b);
       }
     }
-    if (on) {
-      uint16_t* dr = (t == 0 ? dq : dk) + off;
-      *reinterpret_cast<uint2*>(dr + ch_a) = make_uint2(pack_bf16x2(oa[0], oa[1]), pack_bf16x2(oa[2], oa[3]));
-      *reinterpret_cast<uint2*>(dr + ch_b) = make_uint2(pack_bf16x2(ob[0], ob[1]), pack_bf16x2(ob[2], ob[3]));
+#pragma unroll
+    for (int n = 0; n < kBwdRows; ++n) {
+      const int rr = base + 4 * n + sub;
+      const bool on = rr < rows;  // all 16 lanes of a row group share rr
+      const int t = rr < H ? 0 : 1;
+      const int64_t off = token_base + (int64_t)(t == 0 ? rr : rr - H) * kHeadDim;
+      const float x_a[4] = {lo_bf16(xa[n].x), hi_bf16(xa[n].x), lo_bf16(xa[n].y), hi_bf16(xa[n].y)};
+      const float x_b[4] = {lo_bf16(xb[n].x), hi_bf16(xb[n].x), lo_bf16(xb[n].y), hi_bf16(xb[n].y)};
+      const float d_a[4] = {lo_bf16(da[n].x), hi_bf16(da[n].x), lo_bf16(da[n].y), hi_bf16(da[n].y)};
+      const float d_b[4] = {lo_bf16(db[n].x), hi_bf16(db[n].x), lo_bf16(db[n].y), hi_bf16(db[n].y)};
+      float ss = 0.f, tdot = 0.f, ya[4], yb[4], g_a[4], g_b[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ss = fmaf(x_a[e], x_a[e], ss);
+        ss = fmaf(x_b[e], x_b[e], ss);
+        ya[e] = fmaf(d_a[e], cs[e], d_b[e] * sn[e]);    // dy at ch_a (pass-through lanes: cs = 1, sn = 0)
+        yb[e] = fmaf(d_b[e], cs[e], -(d_a[e] * sn[e]));  // dy at ch_b
+        g_a[e] = (t == 0 ? gqa[e] : gka[e]) * ya[e];
+        g_b[e] = (t == 0 ? gqb[e] : gkb[e]) * yb[e];
+        tdot = fmaf(g_a[e], x_a[e], tdot);
+        tdot = fmaf(g_b[e], x_b[e], tdot);
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        ss += __shfl_xor(ss, m, 16);
+        tdot += __shfl_xor(tdot, m, 16);
+      }
+      const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + 1e-5f);
+      const float corr = r * r * r * tdot * (1.0f / kHeadDim);
+      float oa[4], ob[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        oa[e] = fmaf(r, g_a[e], -(x_a[e] * corr));
+        ob[e] = fmaf(r, g_b[e], -(x_b[e] * corr));
+        const float ua = on ? ya[e] * x_a[e] * r : 0.f, ub = on ? yb[e] * x_b[e] * r : 0.f;
+        if (t == 0) {
+          sqa[e] += ua;
+          sqb[e] += ub;
+        } else {
+          ska[e] += ua;
+          skb[e] += ub;
+        }
+      }
+      if (on) {
+        uint16_t* dr = (t == 0 ? dq : dk) + off;
+        *reinterpret_cast<uint2*>(dr + ch_a) = make_uint2(pack_bf16x2(oa[0], oa[1]), pack_bf16x2(oa[2], oa[3]));
+        *reinterpret_cast<uint2*>(dr + ch_b) = make_uint2(pack_bf16x2(ob[0], ob[1]), pack_bf16x2(ob[2], ob[3]));
+      }
     }
   }
   // The four row groups of the wave (lanes i, i+16, i+32, i+48), then the
