@@ -18,22 +18,23 @@
 // split: every output row is produced by exactly one wave, so results do not
 // depend on the grid.
 //
-// Three kernels, each a workgroup of 8 waves owning 256 rows of one head
-// (32 per wave) and streaming the other side through LDS in 64-row tiles:
-//   dq:  rows = queries; streams K and V.  Per tile S^T = K Q^T and
+// Two kernels; each wave owns 32 rows of one head and the workgroup streams
+// the other side through LDS in 64-row tiles:
+//   dq (8 waves, 256 queries): streams K and V.  Per tile S^T = K Q^T and
 //        dP^T = V dO^T (K, V row operands from LDS; Q^T, dO^T held in
 //        registers), dS^T from them, dQ^T += K^T dS^T (K^T gathered by
 //        transposing LDS reads).  It also computes delta for its rows.
-//   dkv<dV>: rows = keys; streams Q, dO and lse.  Per 32-query block
-//        S = Q K^T (Q from LDS, K^T in registers), P, dV^T += dO^T P.
-//   dkv<dK>: the same with dP = dO V^T, dS, dK^T += Q^T dS (also delta).
+//   dkdv (4 waves, 128 keys): streams Q, dO, lse and delta.  Per 32-query
+//        block S = Q K^T and dP = dO V^T (Q, dO from LDS; K^T, V^T in
+//        registers), P and dS, dV^T += dO^T P and dK^T += Q^T dS.
 // Computing the transposed product of the side whose rows the wave owns puts
 // one of its rows in each lane column, so the fp32 accumulators of S (or
 // S^T) convert in place to the bf16 B operand of the next product, in the
 // key (query) order that the transposing reads of the streamed tile produce
-// -- the same layout the forward kernel uses for P^T V.  dK and dV are two
-// launches so that each keeps its accumulators, operands and scores within
-// the 256 registers of two waves per SIMD; they recompute S once more.
+// -- the same layout the forward kernel uses for P^T V.  The dkdv kernel keeps
+// both accumulator sets and both operand sets: one wave per SIMD gives it 512
+// registers (at two waves per SIMD the fused kernel spills; split into a dK
+// and a dV kernel it recomputes S once more and takes 11% longer).
 //
 // Tiles arrive by buffer_load_dwordx4 ... lds into a ring of three slots
 // (no VGPR staging), one barrier per tile; tiles are row-major with chunk c of
@@ -64,7 +65,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;                       // rows a workgroup owns
 constexpr int kTile = 64;                                // rows per streamed tile
 constexpr int kTileBytes = kTile * kD * 2;               // 16 KiB
-constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;  // 1 KiB pieces per wave per tile
 constexpr int kStages = 3;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBufferDword3 = 0x00020000;  // raw buffer, 32-bit data format
@@ -92,15 +92,20 @@ __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >>
 // pieces w and w + 8; slot (row r, physical chunk p) <- row r, channels
 // 8 (p ^ swz(r)) .. +7.  The buffer resource ends at the tensor's last row,
 // so rows past L read as zeros and no address leaves the tensor.
+template <int W>
+constexpr int dma_per_wave() { return kTileBytes / 1024 / W; }  // pieces per wave per tile
+
+template <int W>
 struct DmaOffsets {
-  uint32_t off[kDmaPerWave];
+  uint32_t off[dma_per_wave<W>()];
 };
 
-__device__ __forceinline__ DmaOffsets dma_offsets(int64_t tok_stride, int wave, int lane) {
-  DmaOffsets d;
+template <int W>
+__device__ __forceinline__ DmaOffsets<W> dma_offsets(int64_t tok_stride, int wave, int lane) {
+  DmaOffsets<W> d;
 #pragma unroll
-  for (int it = 0; it < kDmaPerWave; ++it) {
-    const int slot = (it * kWaves + wave) * 64 + lane;
+  for (int it = 0; it < dma_per_wave<W>(); ++it) {
+    const int slot = (it * W + wave) * 64 + lane;
     const int r = slot >> 4;
     const int c = (slot & 15) ^ swz(r);
     d.off[it] = (uint32_t)(((int64_t)r * tok_stride + 8 * c) * 2);
@@ -126,15 +131,16 @@ __device__ __forceinline__ void dma_piece(const i32x4_t& rsrc, uint32_t voff, ui
 }
 
 // Row tile t of the tensor at base (this head's row 0; rows tok_stride
-// elements apart) into LDS at lds_tile: this wave's pieces.
+// elements apart) into LDS at lds_tile: this wave's pieces (W waves share a tile).
+template <int W>
 __device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t tok_stride, int t, int L,
-                                         const DmaOffsets& d, uint32_t lds_tile, int wave) {
+                                         const DmaOffsets<W>& d, uint32_t lds_tile, int wave) {
   const int64_t row_bytes = tok_stride * 2;
   const i32x4_t rsrc = buffer_rsrc(base + (int64_t)t * kTile * tok_stride,
                                    (int64_t)(L - 1 - t * kTile) * row_bytes + kD * 2);
 #pragma unroll
-  for (int it = 0; it < kDmaPerWave; ++it)
-    dma_piece(rsrc, d.off[it], __builtin_amdgcn_readfirstlane(lds_tile + (it * kWaves + wave) * 1024));
+  for (int it = 0; it < dma_per_wave<W>(); ++it)
+    dma_piece(rsrc, d.off[it], __builtin_amdgcn_readfirstlane(lds_tile + (it * W + wave) * 1024));
 }
 
 // The 64 fp32 values v[t*64 .. t*64+63] (zeros past L) into LDS at lds (one
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
   const int n_tiles = (L + kTile - 1) / kTile;
   const lds_char* lds = (const lds_char*)lds_raw;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)lds_raw;
-  const DmaOffsets dmo = dma_offsets(tok_stride, wave, lane);
+  const DmaOffsets<kWaves> dmo = dma_offsets<kWaves>(tok_stride, wave, lane);
   const uint16_t* kh = k + (int64_t)head * kD;
   const uint16_t* vh = v + (int64_t)head * kD;
   auto fill = [&](int t) {
@@ -315,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
           acc[dblk] = mfma32(tr_operand(kt, dblk, 2 * kb + jj, a), ds[jj], acc[dblk]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    dma_wait_all_but<2 * kDmaPerWave>();  // tile t+1 landed (tile t+2 may be in flight)
+    dma_wait_all_but<2 * dma_per_wave<kWaves>()>();  // tile t+1 landed (tile t+2 may be in flight)
     __syncthreads();
   }
   dma_wait();
@@ -323,14 +329,21 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- dk, dv
-// Ring slot: Q tile, dO tile, then 1 KiB of lse and (dK) 1 KiB of delta.
+// Ring slot: Q tile, dO tile, then 1 KiB of lse and 1 KiB of delta.
 constexpr int kSlotBytes = 2 * kTileBytes + 2048;
 
-template <bool kDK>
-__global__ __launch_bounds__(kThreads, 1) void attention_bwd_dkv_kernel(
+// dK and dV in one pass over the queries (S computed once per tile): a
+// workgroup of 4 waves, one per SIMD, owning 128 keys.  With one wave per SIMD
+// a wave has 512 registers, enough for both accumulator sets and both operand
+// sets, which only the matrix cores touch, beside the scores, weights and
+// statistics the vector units work on.
+constexpr int kFusedWaves = 4;
+constexpr int kFusedRows = 32 * kFusedWaves;
+
+__global__ __launch_bounds__(64 * kFusedWaves, 1) void attention_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    uint16_t* __restrict__ res, int L, int H, float c, float scale, int n_full) {
+    uint16_t* __restrict__ dk_out, uint16_t* __restrict__ dv_out, int L, int H, float c, float scale, int n_full) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kStages * kSlotBytes];
   int head, ktile;
   block_tile(blockIdx.x, H, n_full, head, ktile);
@@ -340,7 +353,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dkv_kernel(
   const int n_tiles = (L + kTile - 1) / kTile;
   const lds_char* lds = (const lds_char*)lds_raw;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)lds_raw;
-  const DmaOffsets dmo = dma_offsets(tok_stride, wave, lane);
+  const DmaOffsets<kFusedWaves> dmo = dma_offsets<kFusedWaves>(tok_stride, wave, lane);
   const uint16_t* qh = q + (int64_t)head * kD;
   const uint16_t* doh = dout + (int64_t)head * kD;
   const float* lseh = lse + (int64_t)head * L;
@@ -348,30 +361,28 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dkv_kernel(
   auto fill = [&](int t) {
     const int tt = t < n_tiles ? t : n_tiles - 1;
     const uint32_t s = lds_base + (uint32_t)(t % kStages) * kSlotBytes;
-    dma_rows(qh, tok_stride, tt, L, dmo, s, wave);
-    dma_rows(doh, tok_stride, tt, L, dmo, s + kTileBytes, wave);
+    dma_rows<kFusedWaves>(qh, tok_stride, tt, L, dmo, s, wave);
+    dma_rows<kFusedWaves>(doh, tok_stride, tt, L, dmo, s + kTileBytes, wave);
     if (wave == 0) dma_vec(lseh, tt, L, s + 2 * kTileBytes, lane);
-    if (kDK && wave == 1) dma_vec(dlh, tt, L, s + 2 * kTileBytes + 1024, lane);
-  };
-  // Waves that issue a vector piece have one more DMA per tile in flight.
-  auto wait_all_but_last_tile = [&]() {
-    if (wave == 0 || (kDK && wave == 1)) dma_wait_all_but<2 * kDmaPerWave + 1>();
-    else dma_wait_all_but<2 * kDmaPerWave>();
+    if (wave == 1) dma_vec(dlh, tt, L, s + 2 * kTileBytes + 1024, lane);
   };
   fill(0);
   fill(1);
-
-  const int key = ktile * kRows + wave * 32 + col;
+  const int key = ktile * kFusedRows + wave * 32 + col;
   bf16x8_t kop[8], vop[8];
   load_row_operands(k + (int64_t)head * kD, tok_stride, key, L, g, kop);
-  if (kDK) load_row_operands(v + (int64_t)head * kD, tok_stride, key, L, g, vop);
+  load_row_operands(v + (int64_t)head * kD, tok_stride, key, L, g, vop);
   const Addr a = lds_addresses(lane);
-  f32x16_t acc[4];
+  f32x16_t dka[4], dva[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
+  for (int i = 0; i < 4; ++i) dka[i] = dva[i] = f32x16_t{};
   dma_wait();
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
+    // The accumulators and the K, V operands are read only by the matrix
+    // cores: keep them in the AGPR half.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(dka[i]), "+a"(dva[i]));
     fill(t + 2);
     const lds_char* slot = lds + (t % kStages) * kSlotBytes;
     const lds_char* qt = slot;
@@ -379,43 +390,48 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dkv_kernel(
     const lds_char* vec = slot + 2 * kTileBytes;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      // S = Q K^T (32 queries x this wave's 32 keys); slot 4 rr + qq is query
-      // 32 qb + 8 rr + 4 g + qq of the tile.
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         s = mfma32(row_operand(qt, qb, ks, a), kop[ks], s);
-        if (kDK) dp = mfma32(row_operand(dot, qb, ks, a), vop[ks], dp);
+        dp = mfma32(row_operand(dot, qb, ks, a), vop[ks], dp);
       }
-      float x[16];
+      // Scores are read by the vector units: keep them in VGPRs.
+      asm volatile("" : "+v"(s), "+v"(dp));
+      float xp[16], xs[16];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int r0 = 32 * qb + 8 * rr + 4 * g;
         const f32x4_t l4 = *(const lds_f32x4*)(vec + 4 * r0);
-        f32x4_t d4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (kDK) d4 = *(const lds_f32x4*)(vec + 1024 + 4 * r0);
+        const f32x4_t d4 = *(const lds_f32x4*)(vec + 1024 + 4 * r0);
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const int e = 4 * rr + qq;
           const float p = t * kTile + r0 + qq < L ? __builtin_amdgcn_exp2f(fmaf(s[e], c, -l4[qq] * kLog2e)) : 0.f;
-          x[e] = kDK ? p * (dp[e] - d4[qq]) : p;
+          xp[e] = p;
+          xs[e] = p * (dp[e] - d4[qq]);
         }
       }
-      bf16x8_t w[2];
-      pack_operands(x, w);
-      // dV^T += dO^T P, or dK^T += Q^T dS: A gathered from the tile by
-      // transposing reads in the accumulator's query order.
+      bf16x8_t wp[2], wsv[2];
+      pack_operands(xp, wp);
+      pack_operands(xs, wsv);
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int dblk = 0; dblk < 4; ++dblk)
-          acc[dblk] = mfma32(tr_operand(kDK ? qt : dot, dblk, 2 * qb + jj, a), w[jj], acc[dblk]);
+        for (int dblk = 0; dblk < 4; ++dblk) {
+          dva[dblk] = mfma32(tr_operand(dot, dblk, 2 * qb + jj, a), wp[jj], dva[dblk]);
+          dka[dblk] = mfma32(tr_operand(qt, dblk, 2 * qb + jj, a), wsv[jj], dka[dblk]);
+        }
     }
-    wait_all_but_last_tile();  // tile t+1 landed (tile t+2 may be in flight)
+    if (wave < 2) dma_wait_all_but<2 * dma_per_wave<kFusedWaves>() + 1>();
+    else dma_wait_all_but<2 * dma_per_wave<kFusedWaves>()>();
     __syncthreads();
   }
   dma_wait();
-  if (key < L) store_transposed(res + (int64_t)key * tok_stride + (int64_t)head * kD, acc, kDK ? scale : 1.0f, g);
+  if (key < L) {
+    store_transposed(dk_out + (int64_t)key * tok_stride + (int64_t)head * kD, dka, scale, g);
+    store_transposed(dv_out + (int64_t)key * tok_stride + (int64_t)head * kD, dva, 1.0f, g);
+  }
 }
 
 }  // namespace
@@ -434,12 +450,9 @@ hipError_t launch_attention_backward(const uint16_t* q, const uint16_t* k, const
                      (int)H, c, scale, n_full);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attention_bwd_dkv_kernel<false>, grid, block, 0, stream, q, k, v, dout, lse, delta, dv,
-                     (int)L, (int)H, c, scale, n_full);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attention_bwd_dkv_kernel<true>, grid, block, 0, stream, q, k, v, dout, lse, delta, dk,
-                     (int)L, (int)H, c, scale, n_full);
+  const dim3 fgrid((unsigned)(((L + kFusedRows - 1) / kFusedRows) * (int64_t)H));
+  hipLaunchKernelGGL(attention_bwd_dkdv_kernel, fgrid, dim3(64 * kFusedWaves), 0, stream, q, k, v, dout, lse, delta,
+                     dk, dv, (int)L, (int)H, c, scale, (int)(L / kFusedRows));
   return hipGetLastError();
 }
 
