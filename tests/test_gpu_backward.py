@@ -128,6 +128,24 @@ def test_attention_backward_long_heads(inputs):
     _compare_attention("workload 3", q, k, v, (dq, dk, dv), do_bits, heads=[0, 37])
 
 
+def test_attention_backward_stressed(inputs):
+    """Workload 2 with its stress applied after the prologue: 96 token rows of K'
+    (all heads) times 8 (exact in bf16), which makes a few keys dominate."""
+    inp = inputs(2)
+    q, k, v = _prologue_outputs(inp)
+    k[torch.from_numpy(inp.stress_rows).to(k.device)] *= 8
+    dq, dk, dv, do_bits = _attention_case(q, k, v, 520)
+    _compare_attention("workload 2 stressed", q, k, v, (dq, dk, dv), do_bits, heads=[0, 29, 55])
+
+
+def test_attention_backward_longest(inputs):
+    """L = 28976, H = 7 (one 8-way head share of the 1280x704 video), one head in full."""
+    inp = inputs(4)
+    q, k, v = _prologue_outputs(inp)
+    dq, dk, dv, do_bits = _attention_case(q, k, v, 504)
+    _compare_attention("workload 4", q, k, v, (dq, dk, dv), do_bits, heads=[3])
+
+
 def test_attention_backward_deterministic(inputs):
     inp = inputs(1)
     q, k, v = _prologue_outputs(inp)
