@@ -53,8 +53,11 @@ def prologue_bytes(L: int, H: int) -> float:
 
 
 def kernel_source_sha() -> str:
-    p = os.path.join(ROOT, "packed_full_attention_amd", "csrc", "attention_fwd.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the forward attention kernel's sources (the file and the shared header)."""
+    h = hashlib.sha256()
+    for name in ("attention_fwd.hip", "gfx950_tile.h"):
+        h.update(open(os.path.join(ROOT, "packed_full_attention_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(L: int, H: int):

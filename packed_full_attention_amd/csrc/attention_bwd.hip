@@ -42,22 +42,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gfx950_tile.h"
 #include "h3attn_internal.h"
 
 namespace h3attn {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
-typedef __attribute__((address_space(3))) const f32x4_t lds_f32x4;
 
 constexpr int kD = 128;
 constexpr int kWaves = 8;
@@ -67,26 +56,6 @@ constexpr int kTile = 64;                                // rows per streamed ti
 constexpr int kTileBytes = kTile * kD * 2;               // 16 KiB
 constexpr int kStages = 3;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kBufferDword3 = 0x00020000;  // raw buffer, 32-bit data format
-
-__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  bf16x2_t r;
-  r[0] = (__bf16)a;  // round to nearest even
-  r[1] = (__bf16)b;
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-
 // ---------------------------------------------------------------- tile DMA
 // A 64-row tile of a [L][H][128] tensor: 16 pieces of 1 KiB, wave w writing
 // pieces w and w + 8; slot (row r, physical chunk p) <- row r, channels
@@ -121,15 +90,6 @@ __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, int64_t valid_b
                  (int)__builtin_amdgcn_readfirstlane(n), kBufferDword3};
 }
 
-// 64 lanes x 16 bytes from rsrc + voff (per lane) into LDS at lds (lane order).
-__device__ __forceinline__ void dma_piece(const i32x4_t& rsrc, uint32_t voff, uint32_t lds) {
-  // One wait state between writing M0 and the LDS-DMA instruction that reads it.
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-               :
-               : "v"(voff), "s"(lds), "s"(rsrc)
-               : "memory");
-}
-
 // Row tile t of the tensor at base (this head's row 0; rows tok_stride
 // elements apart) into LDS at lds_tile: this wave's pieces (W waves share a tile).
 template <int W>
@@ -140,20 +100,15 @@ __device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t tok_strid
                                    (int64_t)(L - 1 - t * kTile) * row_bytes + kD * 2);
 #pragma unroll
   for (int it = 0; it < dma_per_wave<W>(); ++it)
-    dma_piece(rsrc, d.off[it], __builtin_amdgcn_readfirstlane(lds_tile + (it * W + wave) * 1024));
+    lds_dma_dwordx4(rsrc, d.off[it], __builtin_amdgcn_readfirstlane(lds_tile + (it * W + wave) * 1024));
 }
 
 // The 64 fp32 values v[t*64 .. t*64+63] (zeros past L) into LDS at lds (one
 // piece: lanes 16..63 read past the 256 valid bytes and write zeros).
 __device__ __forceinline__ void dma_vec(const float* v, int t, int L, uint32_t lds, int lane) {
-  dma_piece(buffer_rsrc(v + (int64_t)t * kTile, (int64_t)(L - t * kTile) * 4), 16u * lane,
-            __builtin_amdgcn_readfirstlane(lds));
+  lds_dma_dwordx4(buffer_rsrc(v + (int64_t)t * kTile, (int64_t)(L - t * kTile) * 4), 16u * lane,
+                  __builtin_amdgcn_readfirstlane(lds));
 }
-
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); }
-template <int n>
-__device__ __forceinline__ void dma_wait_all_but() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(n)); }
 
 // ---------------------------------------------------------------- LDS operands
 // Row operand of a tile (32-row block blk, k-step ks): lane reads row

@@ -87,19 +87,11 @@
 #include <float.h>
 #include <stdint.h>
 
+#include "gfx950_tile.h"
 #include "h3attn_internal.h"
 
 namespace h3attn {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 
 constexpr int kD = 128;
 constexpr int kWaves = 8;                 // waves per workgroup, 32 query rows each
@@ -115,29 +107,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSumBound = 256.0f;        // a lane's tile sum of P above this moves the offset
 
-__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  bf16x2_t r;
-  r[0] = (__bf16)a;  // v_cvt_pk_bf16_f32: round to nearest even
-  r[1] = (__bf16)b;
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-// Reduce over the lane pair (l, l ^ 32): with both operands = x, the swap
-// returns x of the lower half and x of the upper half in every lane.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
 // Key held by row r of a K tile (and by S^T accumulator row r) when V comes
 // transposed: bits 2 and 3 of r swapped.
@@ -151,8 +120,6 @@ __device__ __forceinline__ int perm(int r) { return (r & ~12) | ((r & 4) << 1) |
 // ends at the document's last row: rows past it read as zeros (their scores are
 // masked to -inf and their V rows then contribute nothing), and no address
 // outside the tensor is used.
-constexpr int kBufferDword3 = 0x00020000;  // raw buffer, 32-bit data format
-
 struct DmaOffsets {
   uint32_t off[kDmaPerWave];
 };
@@ -208,27 +175,13 @@ __device__ __forceinline__ TileDma tile_dma(const char* tile_base, int64_t valid
 
 // Issue this wave's DMA piece it (0 .. kDmaPerWave-1) of a tile.
 __device__ __forceinline__ void dma_piece(const TileDma& t, const DmaOffsets& d, int it) {
-  // One wait state between writing M0 and the LDS-DMA instruction that reads it.
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-               :
-               : "v"(d.off[it]), "s"(t.lds + it * kWaves * 1024), "s"(t.rsrc)
-               : "memory");
+  lds_dma_dwordx4(t.rsrc, d.off[it], t.lds + it * kWaves * 1024);
 }
 
 __device__ __forceinline__ void dma_all(const TileDma& t, const DmaOffsets& d) {
 #pragma unroll
   for (int it = 0; it < kDmaPerWave; ++it) dma_piece(t, d, it);
 }
-
-// s_waitcnt immediate for vmcnt(n) (expcnt and lgkmcnt left at their maxima).
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
-// All of this wave's tile DMA has landed in LDS.
-__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); }
-
-// All but this wave's n most recent DMA instructions have landed in LDS.
-template <int n>
-__device__ __forceinline__ void dma_wait_all_but() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(n)); }
 
 // Keeps the compiler from flattening a rarely taken branch into straight-line
 // selects executed on every tile.
@@ -305,10 +258,6 @@ __device__ __forceinline__ void pv(State& st, const bf16x8_t (&p)[4], const lds_
 // The unscheduled form below, for the first tile and the rare path, reads the
 // pair back instead -- the high half as a float is (bits & 0xffff0000), the low
 // half (bits << 16) -- and adds in fp32.
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 
