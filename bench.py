@@ -2,12 +2,15 @@
 over the long single-GPU packed document: L = 16500 tokens (256 text +
 36x15x27 video + 1664 audio), H = 56 heads of 128.
 
-The timed step is the scale-folded form of the path: h3attn_qk_prologue_scaled
-(Q's output carries scale * log2(e), applied before its one bf16 rounding),
-h3attn_v_transpose (V^T, a bit-exact copy) and h3attn_forward_log2 (base-2
-softmax on V^T).  It computes the same attention with the same roundings as
-h3attn_qk_prologue + h3attn_forward, which are timed beside it and reported
-under "plain_path".
+The timed step is the fused, scale-folded form of the path:
+h3attn_k_prologue_table (K's RMSNorm + MM-RoPE in place, and the per-token
+rotation table), h3attn_v_transpose (V^T, a bit-exact copy) and
+h3attn_forward_log2_qprologue (base-2 softmax on V^T, with Q's RMSNorm +
+MM-RoPE and the factor scale * log2(e) applied at the kernel's Q load).  Its
+output is bit-identical to the unfused h3attn_qk_prologue_scaled +
+h3attn_v_transpose + h3attn_forward_log2 ("scale_folded_path") and carries the
+same roundings as h3attn_qk_prologue + h3attn_forward ("plain_path"); both are
+timed beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
                     [--no-cpu-baseline] [--copy-probe]
@@ -15,8 +18,8 @@ under "plain_path".
 Prints one JSON line.  `value` is attention TFLOP/s (4 L^2 128 H per step)
 over the whole step's time; the `roofline` object prices the attention kernel
 alone (HIP events around each launch on the stream it runs on) against the
-dense bf16 matrix-core peak; `prologue` prices the prologue kernel against
-HBM peak; `cpu_baseline` is the fp64 oracle on a bounded sample, timed on
+dense bf16 matrix-core peak; `prologue` prices the standalone Q/K prologue
+kernel (of the unfused path) and `k_prologue` the K-only one against HBM peak; `cpu_baseline` is the fp64 oracle on a bounded sample, timed on
 this host's cores.  Inputs are generated, copied to the GPU and resident in
 HBM before the timed region starts.
 """
@@ -50,6 +53,11 @@ def attention_flops(L: int, H: int) -> float:
 def prologue_bytes(L: int, H: int) -> float:
     # read + write of Q and K (2 B each way per element), 12 B/token positions, 2 x 512 B gammas
     return 8.0 * L * H * 128 + 12.0 * L + 1024.0
+
+
+def k_prologue_bytes(L: int, H: int) -> float:
+    # read + write of K, the 384 B/token rotation table written, positions, gamma_k
+    return 4.0 * L * H * 128 + 384.0 * L + 12.0 * L + 512.0
 
 
 def kernel_source_sha() -> str:
@@ -137,7 +145,8 @@ def main() -> int:
     import numpy as np
     import torch
     from packed_full_attention_amd import (h3attn_attention_backward, h3attn_forward, h3attn_forward_log2,
-                                           h3attn_forward_lse, h3attn_qk_prologue, h3attn_qk_prologue_backward,
+                                           h3attn_forward_log2_qprologue, h3attn_forward_lse,
+                                           h3attn_k_prologue_table, h3attn_qk_prologue, h3attn_qk_prologue_backward,
                                            h3attn_qk_prologue_scaled, h3attn_v_transpose, load_library)
     from packed_full_attention_amd import workloads as wl
 
@@ -183,6 +192,7 @@ def main() -> int:
 
     stream = torch.cuda.current_stream(dev)
     vt = torch.empty(H, 128, (L + 63) // 64 * 64, dtype=torch.bfloat16, device=dev)
+    rope_cs = torch.empty(L, 96, dtype=torch.float32, device=dev)
     K, W = args.steps, args.warmup
     # The prologue rewrites q and k in place, so every step gets its own copy of
     # the generated inputs (made before timing): a step never sees the output of
@@ -201,6 +211,9 @@ def main() -> int:
             b.copy_(k)
         torch.cuda.synchronize()
 
+    fused = [lambda i: h3attn_k_prologue_table(ks[i], gk, pos, rope_cs),
+             lambda i: h3attn_v_transpose(v, vt),
+             lambda i: h3attn_forward_log2_qprologue(qs[i], ks[i], vt, gq, rope_cs, q_scale, out)]
     fast = [lambda i: h3attn_qk_prologue_scaled(qs[i], ks[i], gq, gk, pos, q_scale),
             lambda i: h3attn_v_transpose(v, vt),
             lambda i: h3attn_forward_log2(qs[i], ks[i], vt, out)]
@@ -216,7 +229,12 @@ def main() -> int:
     for i in range(W):
         for f in fast:
             f(i)
-    ms_step, (t_pro, t_vt, t_att), wall_ms = timed(fast, K, W)
+    fast_ms, (t_pro, t_vt_fast, t_att_fast), _ = timed(fast, K, W)
+    refresh()
+    for i in range(W):
+        for f in fused:
+            f(i)
+    ms_step, (t_kpro, t_vt, t_att), wall_ms = timed(fused, K, W)
     del qs, ks
 
     # Training pieces, timed separately (not part of `value`): the forward with
@@ -264,6 +282,7 @@ def main() -> int:
     flops = attention_flops(L, H)
     att_tflops = flops / (t_att * 1e-3) / 1e12
     pro_gbs = prologue_bytes(L, H) / (t_pro * 1e-3) / 1e9
+    kpro_gbs = k_prologue_bytes(L, H) / (t_kpro * 1e-3) / 1e9
     traffic = measured_traffic(L, H)
     mfma_busy, sclk = measured_mfma(L, H)
     result = {
@@ -282,7 +301,8 @@ def main() -> int:
         "config": {"workload": f"packed full attention {w.describe()}, bf16 q/k/v ~N(0,1), "
                                f"gammas 1+0.1N(0,1), seed {1000 + w.index}",
                    "L": L, "H": H, "head_dim": 128, "scale": "1/sqrt(128)"},
-        "roofline": {"bound": "mfma", "kernel": "attention_fwd_kernel<log2>", "achieved": round(att_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "attention_fwd_kernel<log2, Q prologue>",
+                     "achieved": round(att_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(t_att, 4), "mfma_busy_pct": mfma_busy, "sclk_mhz": sclk},
@@ -290,6 +310,13 @@ def main() -> int:
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pro_gbs / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes": prologue_bytes(L, H), "avg_launch_us": round(t_pro * 1e3, 2),
                      "copy_reference_gbs": round(copy_gbs, 1), "frac_of_copy": round(pro_gbs / copy_gbs, 4)},
+        "k_prologue": {"bound": "hbm", "kernel": "qk_prologue_kernel<K only>", "achieved": round(kpro_gbs, 1),
+                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kpro_gbs / PEAK_HBM_GBS, 4),
+                       "algorithmic_bytes": k_prologue_bytes(L, H), "avg_launch_us": round(t_kpro * 1e3, 2)},
+        "scale_folded_path": {"entry_points": "h3attn_qk_prologue_scaled + h3attn_v_transpose + h3attn_forward_log2",
+                              "ms_per_step": round(fast_ms, 4), "attention_ms": round(t_att_fast, 4),
+                              "attention_tflops": round(flops / (t_att_fast * 1e-3) / 1e12, 2),
+                              "v_transpose_us": round(t_vt_fast * 1e3, 2)},
         "v_transpose": {"bound": "hbm", "kernel": "v_transpose_kernel", "avg_launch_us": round(t_vt * 1e3, 2),
                         "achieved": round(2.0 * L * H * 128 * 2 / (t_vt * 1e-3) / 1e9, 1), "unit": "GB/s"},
         "plain_path": {"entry_points": "h3attn_qk_prologue + h3attn_forward", "ms_per_step": round(plain_ms, 4),

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 3
+#define H3ATTN_ABI_VERSION 4
 #define H3ATTN_HEAD_DIM 128
 
 /* Status codes. */
@@ -137,6 +137,42 @@ int64_t h3attn_vt_bytes(int64_t L, int32_t H);
 int h3attn_v_transpose(const void* v, void* vt, int64_t L, int32_t H, hipStream_t stream);
 int h3attn_forward_log2(const void* q, const void* k, const void* vt, void* out, int64_t L,
                         int32_t H, hipStream_t stream);
+
+/*
+ * The same path with Q's prologue fused into the attention kernel's Q load,
+ * as the "h3-metal" README ("Implementation and performance notes",
+ * "Profiling and diagnostic paths") fuses Q/K RMS normalization and RoPE into
+ * the kernel that produces Q and K, with byte-identical results.  Together,
+ *   h3attn_k_prologue_table(k, gamma_k, pos_thw, rope_cs, L, H, s)
+ *   h3attn_v_transpose(v, vt, L, H, s)
+ *   h3attn_forward_log2_qprologue(q, k, vt, out, gamma_q, rope_cs, L, H, q_scale, s)
+ * give the same out, bit for bit, as h3attn_qk_prologue_scaled(..., q_scale,
+ * s) + h3attn_v_transpose + h3attn_forward_log2, and the same k; q is only
+ * read.  Q's prologue output never goes to memory (one write and one read of
+ * Q fewer), and its rotation reuses the per-token table K's prologue writes.
+ *
+ * h3attn_rope_table_bytes: L * 96 * 4 (-1 for an (L, H) the calls reject).
+ *
+ * h3attn_k_prologue_table: h3attn_qk_prologue on k alone (in place, same
+ *   bits), and rope_cs[l][a] = cos(phi_a), rope_cs[l][48 + a] = sin(phi_a)
+ *   for the 48 angles phi_a of token l (fp32 [L][96], as the prologue
+ *   evaluates them).  rope_cs: caller-owned device memory of
+ *   h3attn_rope_table_bytes(L, H) bytes, 16-byte aligned, not overlapping k.
+ *
+ * h3attn_forward_log2_qprologue: h3attn_forward_log2 of q' = the scaled
+ *   prologue of the raw q (as h3attn_qk_prologue_scaled computes it with
+ *   gamma_q, the positions behind rope_cs and q_scale), k from
+ *   h3attn_k_prologue_table, vt from h3attn_v_transpose.  q: raw bf16
+ *   [L][H][128], not modified; gamma_q fp32 [128] and rope_cs 16-byte
+ *   aligned; q_scale finite and > 0 (scale * log2(e) for softmax scale
+ *   `scale`); out must not overlap q, k, vt, gamma_q or rope_cs.
+ */
+int64_t h3attn_rope_table_bytes(int64_t L, int32_t H);
+int h3attn_k_prologue_table(void* k, const float* gamma_k, const int32_t* pos_thw, float* rope_cs,
+                            int64_t L, int32_t H, hipStream_t stream);
+int h3attn_forward_log2_qprologue(const void* q, const void* k, const void* vt, void* out,
+                                  const float* gamma_q, const float* rope_cs, int64_t L, int32_t H,
+                                  float q_scale, hipStream_t stream);
 
 /*
  * Training: the backward pass ("MiniMax-H3 WS1/WS2 kernel roadmap" RFC,

@@ -21,6 +21,7 @@ EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward", "h3attn_qk_prologue_
                     "h3attn_v_transpose", "h3attn_forward_log2", "h3attn_forward_lse",
                     "h3attn_attention_backward_workspace_bytes", "h3attn_attention_backward",
                     "h3attn_qk_prologue_backward_workspace_bytes", "h3attn_qk_prologue_backward",
+                    "h3attn_rope_table_bytes", "h3attn_k_prologue_table", "h3attn_forward_log2_qprologue",
                     "h3attn_strerror", "h3attn_last_error", "h3attn_abi_version")
 
 _lock = threading.Lock()
@@ -66,6 +67,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.h3attn_qk_prologue_backward_workspace_bytes.restype = i64
         lib.h3attn_qk_prologue_backward.argtypes = [vp] * 10 + [i64, i32, vp]
         lib.h3attn_qk_prologue_backward.restype = ctypes.c_int
+        lib.h3attn_rope_table_bytes.argtypes = [i64, i32]
+        lib.h3attn_rope_table_bytes.restype = i64
+        lib.h3attn_k_prologue_table.argtypes = [vp, vp, vp, vp, i64, i32, vp]
+        lib.h3attn_k_prologue_table.restype = ctypes.c_int
+        lib.h3attn_forward_log2_qprologue.argtypes = [vp] * 6 + [i64, i32, ctypes.c_float, vp]
+        lib.h3attn_forward_log2_qprologue.restype = ctypes.c_int
         lib.h3attn_strerror.argtypes = [ctypes.c_int]
         lib.h3attn_strerror.restype = ctypes.c_char_p
         lib.h3attn_last_error.argtypes = []
@@ -191,6 +198,49 @@ def h3attn_forward_log2(q, k, vt, out=None):
     """Base-2 softmax attention (q carries the softmax scale times log2(e); V as vt from
     h3attn_v_transpose); returns out."""
     return _forward("h3attn_forward_log2", q, k, vt, out, None)
+
+
+def h3attn_k_prologue_table(k, gamma_k, pos_thw, rope_cs=None):
+    """In-place prologue of k alone (the bits h3attn_qk_prologue gives it) plus the
+    per-token rotation table rope_cs, fp32 [L, 96] (cosines, then sines); returns rope_cs."""
+    import torch
+    L, H = _lh(k)
+    dev = k.device
+    _check_tensor("k", k, torch.bfloat16, (L, H, HEAD_DIM))
+    _check_tensor("gamma_k", gamma_k, torch.float32, (HEAD_DIM,), dev)
+    _check_tensor("pos_thw", pos_thw, torch.int32, (L, 3), dev)
+    if rope_cs is None:
+        rope_cs = torch.empty(L, 96, dtype=torch.float32, device=dev)
+    _check_tensor("rope_cs", rope_cs, torch.float32, (L, 96), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.h3attn_k_prologue_table(k.data_ptr(), gamma_k.data_ptr(), pos_thw.data_ptr(), rope_cs.data_ptr(),
+                                         L, H, torch.cuda.current_stream(dev).cuda_stream)
+    _raise_on(lib, "h3attn_k_prologue_table", st)
+    return rope_cs
+
+
+def h3attn_forward_log2_qprologue(q, k, vt, gamma_q, rope_cs, q_scale: float, out=None):
+    """h3attn_forward_log2 with Q's prologue (gamma_q, rope_cs, q_scale) applied inside
+    the attention kernel to the raw q, which is not modified; returns out."""
+    import torch
+    L, H = _lh(q)
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, (L, H, HEAD_DIM))
+    _check_tensor("k", k, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    _check_tensor("vt", vt, torch.bfloat16, (H, HEAD_DIM, padded_length(L)), dev)
+    _check_tensor("gamma_q", gamma_q, torch.float32, (HEAD_DIM,), dev)
+    _check_tensor("rope_cs", rope_cs, torch.float32, (L, 96), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.h3attn_forward_log2_qprologue(q.data_ptr(), k.data_ptr(), vt.data_ptr(), out.data_ptr(),
+                                               gamma_q.data_ptr(), rope_cs.data_ptr(), L, H, float(q_scale),
+                                               torch.cuda.current_stream(dev).cuda_stream)
+    _raise_on(lib, "h3attn_forward_log2_qprologue", st)
+    return out
 
 
 def h3attn_forward_lse(q, k, v, out=None, lse=None, scale: Optional[float] = None):

@@ -512,10 +512,79 @@ __device__ __forceinline__ void stream_only(const Ctx& x) {
   dma_wait();
 }
 
-template <bool kLog2, bool kVT>
+// Q's RMSNorm and MM-RoPE, applied to the raw Q^T operand as it is loaded
+// (the Q half of the fused prologue, same RFC, section 5 items
+// h3_qk_rmsnorm_d128 and h3_mm_rope_3axis_partial):
+//   y_c = x_c (mean(x^2) + 1e-5)^(-1/2) (gamma_c q_scale)
+//   out_c = y_c cos phi_c - y_{c+48} sin phi_c, out_{c+48} = y_{c+48} cos phi_c
+//   + y_c sin phi_c (c < 48), out_c = y_c (c >= 96), rounded once to bf16.
+// Every fp32 operation follows the standalone prologue kernel in value and
+// order, so q comes out with the same bits.  That kernel gives a head-row to
+// 16 lanes: lane i holds channels 4i..4i+3 and 48+4i..48+4i+3 (i < 12) or
+// pass-through channels, and adds its 8 squares in that order.  Those channels
+// sit in lane half (i >> 1) & 1 here, so half g holds the 8 lanes
+// i = 4m + 2g + o: channels 16m + 8g + 4o.. of q[m] and q[m+3] for m < 3, of
+// q[6] and q[7] for m = 3.  Its butterfly (xor 1, 2, 4, 8 over i) is then:
+// xor 1 (over o) and xor 4, 8 (over m) inside the lane, xor 2 the exchange
+// between the two halves.  IEEE addition commutes, so every partner order
+// gives the same sum.  cs_row: the row's cosines (48) then sines (48).
+__device__ __forceinline__ void q_prologue(bf16x8_t (&q)[8], int g, const float* __restrict__ gamma_q,
+                                           const float* __restrict__ cs_row, float q_scale) {
+  f32x4_t gm[8][2], cs[3][2], sn[3][2];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) gm[ks][h] = *reinterpret_cast<const f32x4_t*>(gamma_q + 16 * ks + 8 * g + 4 * h);
+#pragma unroll
+  for (int m = 0; m < 3; ++m)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      cs[m][h] = *reinterpret_cast<const f32x4_t*>(cs_row + 16 * m + 8 * g + 4 * h);
+      sn[m][h] = *reinterpret_cast<const f32x4_t*>(cs_row + 48 + 16 * m + 8 * g + 4 * h);
+    }
+  float s[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int ka = m < 3 ? m : 6, kb = m < 3 ? m + 3 : 7;
+    float part[2];
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      float ss = (float)q[ka][4 * o] * (float)q[ka][4 * o];
+#pragma unroll
+      for (int e = 1; e < 4; ++e) ss = fmaf((float)q[ka][4 * o + e], (float)q[ka][4 * o + e], ss);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = fmaf((float)q[kb][4 * o + e], (float)q[kb][4 * o + e], ss);
+      part[o] = ss;
+    }
+    s[m] = pair_sum(part[0] + part[1]);
+  }
+  const float ss = (s[0] + s[1]) + (s[2] + s[3]);
+  const float r = 1.0f / sqrtf(ss * (1.0f / kD) + 1e-5f);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int ka = m < 3 ? m : 6, kb = m < 3 ? m + 3 : 7;
+    bf16x8_t oa, ob;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float c = m < 3 ? cs[m][e >> 2][e & 3] : 1.0f;
+      const float sv = m < 3 ? sn[m][e >> 2][e & 3] : 0.0f;
+      const float ya = (float)q[ka][e] * r * (gm[ka][e >> 2][e & 3] * q_scale);
+      const float yb = (float)q[kb][e] * r * (gm[kb][e >> 2][e & 3] * q_scale);
+      oa[e] = (__bf16)fmaf(ya, c, -(yb * sv));  // round to nearest even
+      ob[e] = (__bf16)fmaf(yb, c, ya * sv);
+    }
+    q[ka] = oa;
+    q[kb] = ob;
+  }
+}
+
+// kQPro: q holds the raw (pre-prologue) rows and q_prologue is applied at
+// the load, with gamma_q, the rope_cs table ([L][96] fp32) and q_scale.
+template <bool kLog2, bool kVT, bool kQPro>
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int L, int H, int Lp, float scale_log2e, int n_qfull) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int L, int H, int Lp, float scale_log2e, int n_qfull,
+    const float* __restrict__ gamma_q, const float* __restrict__ rope_cs, float q_scale) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStages * kTileBytes];
 
   // Blocks are dispatched in increasing order, round-robin over the 8 XCDs
@@ -596,6 +665,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     const uint16_t* p = q + (int64_t)qrow * tok_stride + (int64_t)head * kD + 8 * x.g;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) st.q[ks] = *reinterpret_cast<const bf16x8_t*>(p + 16 * ks);
+    if (kQPro) q_prologue(st.q, x.g, gamma_q, rope_cs + (int64_t)qrow * 96, q_scale);
   } else {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) st.q[ks] = bf16x8_t{};
@@ -742,11 +812,21 @@ hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const 
   const int n_qfull = (int)(L / kBM);  // full 256-row q-tiles per head
   const dim3 grid((unsigned)attention_grid_blocks(L, H));
   if (log2)  // v is V^T
-    hipLaunchKernelGGL((attention_fwd_kernel<true, true>), grid, dim3(kThreads), 0, stream, q, k, v, out, lse,
-                       (int)L, (int)H, (int)vt_padded_length(L), 1.0f, n_qfull);
+    hipLaunchKernelGGL((attention_fwd_kernel<true, true, false>), grid, dim3(kThreads), 0, stream, q, k, v, out,
+                       lse, (int)L, (int)H, (int)vt_padded_length(L), 1.0f, n_qfull, nullptr, nullptr, 1.0f);
   else
-    hipLaunchKernelGGL((attention_fwd_kernel<false, false>), grid, dim3(kThreads), 0, stream, q, k, v, out, lse,
-                       (int)L, (int)H, 0, scale * kLog2e, n_qfull);
+    hipLaunchKernelGGL((attention_fwd_kernel<false, false, false>), grid, dim3(kThreads), 0, stream, q, k, v, out,
+                       lse, (int)L, (int)H, 0, scale * kLog2e, n_qfull, nullptr, nullptr, 1.0f);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_forward_qprologue(const uint16_t* q_raw, const uint16_t* k, const uint16_t* vt,
+                                              uint16_t* out, const float* gamma_q, const float* rope_cs,
+                                              int64_t L, int32_t H, float q_scale, hipStream_t stream) {
+  const int n_qfull = (int)(L / kBM);
+  hipLaunchKernelGGL((attention_fwd_kernel<true, true, true>), dim3((unsigned)attention_grid_blocks(L, H)),
+                     dim3(kThreads), 0, stream, q_raw, k, vt, out, nullptr, (int)L, (int)H,
+                     (int)vt_padded_length(L), 1.0f, n_qfull, gamma_q, rope_cs, q_scale);
   return hipGetLastError();
 }
 

@@ -163,6 +163,55 @@ int h3attn_forward_lse(const void* q, const void* k, const void* v, void* out, f
   return forward(q, k, v, out, L, H, scale, false, stream, lse);
 }
 
+int64_t h3attn_rope_table_bytes(int64_t L, int32_t H) {
+  uint64_t bytes = 0;
+  if (check_shape(L, H, &bytes) != H3A_OK) return -1;
+  ok();
+  return L * 96 * 4;
+}
+
+int h3attn_k_prologue_table(void* k, const float* gamma_k, const int32_t* pos_thw, float* rope_cs, int64_t L,
+                            int32_t H, hipStream_t stream) {
+  if (!k || !gamma_k || !pos_thw || !rope_cs) return fail(H3A_EINVAL, "null pointer argument%s");
+  uint64_t bytes = 0;
+  if (int s = check_shape(L, H, &bytes)) return s;
+  if (!aligned(k, 16) || !aligned(rope_cs, 16)) return fail(H3A_EINVAL, "k and rope_cs must be 16-byte aligned%s");
+  if (!aligned(gamma_k, 4) || !aligned(pos_thw, 4))
+    return fail(H3A_EINVAL, "gamma_k and pos_thw must be 4-byte aligned%s");
+  const uint64_t tbytes = (uint64_t)L * 96 * 4;
+  if (overlap(rope_cs, tbytes, k, bytes) || overlap(rope_cs, tbytes, gamma_k, 512) ||
+      overlap(rope_cs, tbytes, pos_thw, (uint64_t)L * 12))
+    return fail(H3A_EINVAL, "rope_cs overlaps k, gamma_k or pos_thw%s");
+  if (h3attn::prologue_grid_blocks(L) * 256 >= kMaxThreadsPerGrid)
+    return fail(H3A_EUNSUPPORTED, "prologue grid too large for L%s");
+  const hipError_t e =
+      h3attn::launch_k_prologue(static_cast<uint16_t*>(k), gamma_k, pos_thw, rope_cs, L, H, stream);
+  if (e != hipSuccess) return fail(H3A_EHIP, "prologue launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int h3attn_forward_log2_qprologue(const void* q, const void* k, const void* vt, void* out, const float* gamma_q,
+                                  const float* rope_cs, int64_t L, int32_t H, float q_scale, hipStream_t stream) {
+  if (!q || !k || !vt || !out || !gamma_q || !rope_cs) return fail(H3A_EINVAL, "null pointer argument%s");
+  uint64_t bytes = 0;
+  if (int s = check_shape(L, H, &bytes)) return s;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(vt, 16) || !aligned(out, 16) || !aligned(gamma_q, 16) ||
+      !aligned(rope_cs, 16))
+    return fail(H3A_EINVAL, "q, k, vt, out, gamma_q and rope_cs must be 16-byte aligned%s");
+  if (!(isfinite(q_scale) && q_scale > 0.0f)) return fail(H3A_EINVAL, "q_scale must be finite and > 0%s");
+  const uint64_t vbytes = (uint64_t)h3attn::vt_bytes(L, H), tbytes = (uint64_t)L * 96 * 4;
+  if (overlap(out, bytes, q, bytes) || overlap(out, bytes, k, bytes) || overlap(out, bytes, vt, vbytes) ||
+      overlap(out, bytes, gamma_q, 512) || overlap(out, bytes, rope_cs, tbytes))
+    return fail(H3A_EINVAL, "out overlaps q, k, vt, gamma_q or rope_cs%s");
+  if (h3attn::attention_grid_blocks(L, H) * h3attn::attention_block_threads() >= kMaxThreadsPerGrid)
+    return fail(H3A_EUNSUPPORTED, "attention grid too large for (L, H)%s");
+  const hipError_t e = h3attn::launch_attention_forward_qprologue(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(vt),
+      static_cast<uint16_t*>(out), gamma_q, rope_cs, L, H, q_scale, stream);
+  if (e != hipSuccess) return fail(H3A_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int64_t h3attn_attention_backward_workspace_bytes(int64_t L, int32_t H) {
   uint64_t bytes = 0;
   if (check_shape(L, H, &bytes) != H3A_OK) return -1;

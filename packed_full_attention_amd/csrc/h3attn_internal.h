@@ -13,6 +13,11 @@ hipError_t launch_qk_prologue(uint16_t* q, uint16_t* k, const float* gamma_q,
                               const float* gamma_k, const int32_t* pos, int64_t L, int32_t H,
                               float q_scale, hipStream_t stream);
 
+// The prologue on K alone (in place), plus each token's rotation table
+// rope_cs ([L][96] fp32: cos of angles 0..47, then their sines).
+hipError_t launch_k_prologue(uint16_t* k, const float* gamma_k, const int32_t* pos, float* rope_cs, int64_t L,
+                             int32_t H, hipStream_t stream);
+
 // Enqueue the flash-attention forward kernel.  log2 = false: weights
 // exp(scale <q,k>), v row-major [L][H][128]; log2 = true: weights 2^<q,k>
 // (q already carries the softmax scale times log2(e)), scale ignored, and v
@@ -21,6 +26,15 @@ hipError_t launch_qk_prologue(uint16_t* q, uint16_t* k, const float* gamma_q,
 hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                     uint16_t* out, float* lse, int64_t L, int32_t H, float scale, bool log2,
                                     hipStream_t stream);
+
+// The log2 variant with Q's prologue applied at its Q load: q_raw holds the
+// raw rows, gamma_q (16-byte aligned) and rope_cs ([L][96] fp32, as written by
+// launch_k_prologue) supply the RMSNorm weights and the rotation; q_scale as
+// in launch_qk_prologue.  Same result bits as launch_qk_prologue followed by
+// the log2 variant.
+hipError_t launch_attention_forward_qprologue(const uint16_t* q_raw, const uint16_t* k, const uint16_t* vt,
+                                              uint16_t* out, const float* gamma_q, const float* rope_cs,
+                                              int64_t L, int32_t H, float q_scale, hipStream_t stream);
 
 // Enqueue the attention backward (three kernels, in this order): dq and the
 // per-row delta = <dout, out> (fp32 [H][L], written), then dv, then dk.

@@ -48,11 +48,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-template <int kPassesPerChunk>
+// kKOnly: only K's rows, and the lane's cosines and sines go to rope_cs
+// (fp32 [L][96]: cos of the token's 48 angles, then their sines) for an
+// attention kernel that applies Q's prologue itself.
+template <int kPassesPerChunk, bool kKOnly>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
     uint16_t* __restrict__ q, uint16_t* __restrict__ k, const float* __restrict__ gamma_q,
     const float* __restrict__ gamma_k, const int32_t* __restrict__ pos, int64_t L, int32_t H,
-    float q_scale) {
+    float q_scale, float* __restrict__ rope_cs) {
   const int lane = threadIdx.x & 63;
   const int64_t token = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (token >= L) return;  // whole wave exits together
@@ -83,9 +86,13 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
       const float inv_freq = 1.0f / powf(10000.0f, (float)(2 * j) / 32.0f);
       sincosf(p * inv_freq, &sn[e], &cs[e]);
     }
+    if (kKOnly && sub == 0) {  // angles 4i .. 4i+3 of the token
+      *reinterpret_cast<float4*>(rope_cs + token * 96 + 4 * i) = make_float4(cs[0], cs[1], cs[2], cs[3]);
+      *reinterpret_cast<float4*>(rope_cs + token * 96 + 48 + 4 * i) = make_float4(sn[0], sn[1], sn[2], sn[3]);
+    }
   }
 
-  const int rows = 2 * H;  // Q rows 0..H-1, then K rows
+  const int rows = kKOnly ? H : 2 * H;  // Q rows 0..H-1, then K rows (K only: K rows 0..H-1)
   const int64_t token_base = token * (int64_t)H * kHeadDim;
   for (int r0 = 0; r0 < rows; r0 += 4 * kPassesPerChunk) {
     uint2 va[kPassesPerChunk], vb[kPassesPerChunk];
@@ -95,7 +102,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
       va[ps] = make_uint2(0u, 0u);
       vb[ps] = make_uint2(0u, 0u);
       if (rr < rows) {
-        const uint16_t* row = (rr < H ? q : k) + token_base + (int64_t)(rr < H ? rr : rr - H) * kHeadDim;
+        const bool rq = !kKOnly && rr < H;
+        const uint16_t* row = (rq ? q : k) + token_base + (int64_t)(kKOnly || rq ? rr : rr - H) * kHeadDim;
         va[ps] = *reinterpret_cast<const uint2*>(row + ch_a);
         vb[ps] = *reinterpret_cast<const uint2*>(row + ch_b);
       }
@@ -116,7 +124,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
       ss += __shfl_xor(ss, 4, 16);
       ss += __shfl_xor(ss, 8, 16);
       const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + 1e-5f);
-      const bool is_q = rr < H;
+      const bool is_q = !kKOnly && rr < H;
       float oa[4], ob[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -126,7 +134,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
         ob[e] = fmaf(yb, cs[e], ya * sn[e]);
       }
       if (rr < rows) {
-        uint16_t* row = (is_q ? q : k) + token_base + (int64_t)(is_q ? rr : rr - H) * kHeadDim;
+        uint16_t* row = (is_q ? q : k) + token_base + (int64_t)(kKOnly || is_q ? rr : rr - H) * kHeadDim;
         *reinterpret_cast<uint2*>(row + ch_a) = make_uint2(pack_bf16x2(oa[0], oa[1]), pack_bf16x2(oa[2], oa[3]));
         *reinterpret_cast<uint2*>(row + ch_b) = make_uint2(pack_bf16x2(ob[0], ob[1]), pack_bf16x2(ob[2], ob[3]));
       }
@@ -311,33 +319,49 @@ __global__ __launch_bounds__(2 * kHeadDim) void gamma_final_kernel(const float* 
 
 int64_t prologue_grid_blocks(int64_t L) { return (L + kWavesPerBlock - 1) / kWavesPerBlock; }
 
-// Passes per chunk for 2H rows: the candidate whose chunks leave the fewest
-// row slots empty, the larger on a tie.
-static int prologue_passes(int32_t H) {
+// Passes per chunk for n rows a token: the candidate whose chunks leave the
+// fewest row slots empty, the larger on a tie.
+static int prologue_passes(int64_t n) {
   const int candidates[3] = {14, 8, 4};
   int best = 14;
   int64_t best_waste = -1;
   for (int p : candidates) {
-    const int64_t rows = 4 * p, waste = (2 * (int64_t)H + rows - 1) / rows * rows - 2 * (int64_t)H;
+    const int64_t rows = 4 * p, waste = (n + rows - 1) / rows * rows - n;
     if (best_waste < 0 || waste < best_waste) best = p, best_waste = waste;
   }
   return best;
 }
 
-hipError_t launch_qk_prologue(uint16_t* q, uint16_t* k, const float* gamma_q, const float* gamma_k,
-                              const int32_t* pos, int64_t L, int32_t H, float q_scale, hipStream_t stream) {
+template <bool kKOnly>
+static void launch_prologue(uint16_t* q, uint16_t* k, const float* gamma_q, const float* gamma_k,
+                            const int32_t* pos, int64_t L, int32_t H, float q_scale, float* rope_cs,
+                            hipStream_t stream) {
   const dim3 grid((unsigned)prologue_grid_blocks(L)), block(kWavesPerBlock * 64);
-  switch (prologue_passes(H)) {
+  switch (prologue_passes(kKOnly ? H : 2 * (int64_t)H)) {
     case 14:
-      hipLaunchKernelGGL(qk_prologue_kernel<14>, grid, block, 0, stream, q, k, gamma_q, gamma_k, pos, L, H, q_scale);
+      hipLaunchKernelGGL((qk_prologue_kernel<14, kKOnly>), grid, block, 0, stream, q, k, gamma_q, gamma_k, pos, L,
+                         H, q_scale, rope_cs);
       break;
     case 8:
-      hipLaunchKernelGGL(qk_prologue_kernel<8>, grid, block, 0, stream, q, k, gamma_q, gamma_k, pos, L, H, q_scale);
+      hipLaunchKernelGGL((qk_prologue_kernel<8, kKOnly>), grid, block, 0, stream, q, k, gamma_q, gamma_k, pos, L,
+                         H, q_scale, rope_cs);
       break;
     default:
-      hipLaunchKernelGGL(qk_prologue_kernel<4>, grid, block, 0, stream, q, k, gamma_q, gamma_k, pos, L, H, q_scale);
+      hipLaunchKernelGGL((qk_prologue_kernel<4, kKOnly>), grid, block, 0, stream, q, k, gamma_q, gamma_k, pos, L,
+                         H, q_scale, rope_cs);
       break;
   }
+}
+
+hipError_t launch_qk_prologue(uint16_t* q, uint16_t* k, const float* gamma_q, const float* gamma_k,
+                              const int32_t* pos, int64_t L, int32_t H, float q_scale, hipStream_t stream) {
+  launch_prologue<false>(q, k, gamma_q, gamma_k, pos, L, H, q_scale, nullptr, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_k_prologue(uint16_t* k, const float* gamma_k, const int32_t* pos, float* rope_cs, int64_t L,
+                             int32_t H, hipStream_t stream) {
+  launch_prologue<true>(nullptr, k, gamma_k, gamma_k, pos, L, H, 1.0f, rope_cs, stream);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ def test_header_declares_the_expected_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.h3attn_abi_version() == 3
+    assert lib.h3attn_abi_version() == 4
 
 
 def test_strerror_strings(lib):
@@ -106,6 +106,36 @@ def test_scaled_entry_points_reject(lib):
     t = lambda **kw: lib.h3attn_v_transpose(kw.get("v", A), kw.get("vt", B), kw.get("L", 160), 4, None)
     assert t(v=None) == 1 and t(vt=None) == 1 and t(L=0) == 1 and t(vt=B + 4) == 1
     assert t(vt=A + 1024) == 1 and "overlap" in lib.h3attn_last_error().decode()
+
+
+def test_fused_entry_points_reject(lib):
+    kp = lambda **kw: lib.h3attn_k_prologue_table(kw.get("k", B), kw.get("gk", G), kw.get("pos", P),
+                                                  kw.get("cs", C), kw.get("L", 160), kw.get("H", 4), None)
+    for kw in (dict(k=None), dict(gk=None), dict(pos=None), dict(cs=None)):
+        assert kp(**kw) == 1 and "null" in lib.h3attn_last_error().decode()
+    assert kp(L=0) == 1 and kp(H=0) == 1
+    assert kp(cs=C + 4) == 1 and "aligned" in lib.h3attn_last_error().decode()
+    assert kp(k=B + 8) == 1 and kp(pos=P + 2) == 1
+    assert kp(cs=B + 1024) == 1 and "overlap" in lib.h3attn_last_error().decode()
+    assert kp(cs=P - 256) == 1 and "overlap" in lib.h3attn_last_error().decode()
+    fq = lambda **kw: lib.h3attn_forward_log2_qprologue(kw.get("q", A), B, kw.get("vt", C), kw.get("out", O),
+                                                        kw.get("gq", G), kw.get("cs", P), kw.get("L", 160), 4,
+                                                        kw.get("s", 0.1275), None)
+    for kw in (dict(q=None), dict(vt=None), dict(out=None), dict(gq=None), dict(cs=None)):
+        assert fq(**kw) == 1 and "null" in lib.h3attn_last_error().decode()
+    assert fq(gq=G + 4) == 1 and "aligned" in lib.h3attn_last_error().decode()
+    assert fq(cs=P + 8) == 1 and "aligned" in lib.h3attn_last_error().decode()
+    for s_ in (0.0, -1.0, float("nan"), float("inf")):
+        assert fq(s=s_) == 1 and "q_scale" in lib.h3attn_last_error().decode()
+    for out in (A, B + 256, C + 1024, G - 256, P + 4096):
+        assert fq(out=out) == 1 and "overlap" in lib.h3attn_last_error().decode()
+    assert fq(L=1 << 31) == 2
+
+
+@pytest.mark.parametrize("L,H,want", [(160, 4, 160 * 384), (1, 56, 384), (16500, 56, 16500 * 384), (0, 4, -1),
+                                      (8, 0, -1)])
+def test_rope_table_bytes(lib, L, H, want):
+    assert lib.h3attn_rope_table_bytes(L, H) == want
 
 
 @pytest.mark.parametrize("L,H,want", [
