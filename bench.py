@@ -246,7 +246,7 @@ def main() -> int:
     dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
     out2, lse = torch.empty_like(q), torch.empty(H, L, dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = torch.empty(L * H * 4, dtype=torch.uint8, device=dev)
+    ws = torch.empty(int(load_library().h3attn_attention_backward_workspace_bytes(L, H)), dtype=torch.uint8, device=dev)
     pws = torch.empty(int(load_library().h3attn_qk_prologue_backward_workspace_bytes(L, H)), dtype=torch.uint8,
                       device=dev)
     dgq, dgk = torch.empty(128, device=dev), torch.empty(128, device=dev)

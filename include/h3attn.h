@@ -191,9 +191,10 @@ int h3attn_forward_log2_qprologue(const void* q, const void* k, const void* vt, 
  *   i.e. after the prologue); lse: that forward's lse; dq, dk, dv: bf16
  *   [L][H][128] outputs (fp32 accumulation, one rounding); workspace:
  *   caller-owned device memory of h3attn_attention_backward_workspace_bytes(L, H)
- *   bytes (it receives delta, fp32 [H][L]).  All 16-byte aligned (lse, the
+ *   bytes (it receives per-row statistics: -lse log2(e) and -delta, fp32
+ *   [2][H][Lp], Lp = L rounded up to a multiple of 64).  All 16-byte aligned (lse, the
  *   workspace: 4); the outputs and the workspace must not overlap one another
- *   or any input.  Three launches on `stream`; deterministic (no atomics, no
+ *   or any input.  Two launches on `stream`; deterministic (no atomics, no
  *   split: one wave produces each output row).
  *
  * h3attn_qk_prologue_backward: given dq, dk = the gradients with respect to

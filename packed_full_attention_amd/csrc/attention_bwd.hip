@@ -23,10 +23,12 @@
 //   dq (8 waves, 256 queries): streams K and V.  Per tile S^T = K Q^T and
 //        dP^T = V dO^T (K, V row operands from LDS; Q^T, dO^T held in
 //        registers), dS^T from them, dQ^T += K^T dS^T (K^T gathered by
-//        transposing LDS reads).  It also computes delta for its rows.
-//   dkdv (4 waves, 128 keys): streams Q, dO, lse and delta.  Per 32-query
-//        block S = Q K^T and dP = dO V^T (Q, dO from LDS; K^T, V^T in
-//        registers), P and dS, dV^T += dO^T P and dK^T += Q^T dS.
+//        transposing LDS reads).  It also computes delta for its rows and
+//        leaves -lse log2(e) and -delta per row for the second kernel.
+//   dkdv (4 waves, 128 keys): streams Q, dO and those two statistics.  Per
+//        32-query block S = Q K^T and dP - delta = dO V^T - delta (Q, dO from
+//        LDS; K^T, V^T in registers), P and dS, dV^T += dO^T P and
+//        dK^T += Q^T dS, software-pipelined over the blocks.
 // Computing the transposed product of the side whose rows the wave owns puts
 // one of its rows in each lane column, so the fp32 accumulators of S (or
 // S^T) convert in place to the bf16 B operand of the next product, in the
@@ -90,23 +92,29 @@ __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, int64_t valid_b
                  (int)__builtin_amdgcn_readfirstlane(n), kBufferDword3};
 }
 
-// Row tile t of the tensor at base (this head's row 0; rows tok_stride
-// elements apart) into LDS at lds_tile: this wave's pieces (W waves share a tile).
+// Piece it of this wave's share of row tile t of the tensor at base (this
+// head's row 0; rows tok_stride elements apart) into LDS at lds_tile (W waves
+// share a tile, dma_per_wave<W>() pieces each).
 template <int W>
-__device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t tok_stride, int t, int L,
-                                         const DmaOffsets<W>& d, uint32_t lds_tile, int wave) {
+__device__ __forceinline__ void dma_row_piece(const uint16_t* base, int64_t tok_stride, int t, int L,
+                                              const DmaOffsets<W>& d, uint32_t lds_tile, int wave, int it) {
   const int64_t row_bytes = tok_stride * 2;
   const i32x4_t rsrc = buffer_rsrc(base + (int64_t)t * kTile * tok_stride,
                                    (int64_t)(L - 1 - t * kTile) * row_bytes + kD * 2);
-#pragma unroll
-  for (int it = 0; it < dma_per_wave<W>(); ++it)
-    lds_dma_dwordx4(rsrc, d.off[it], __builtin_amdgcn_readfirstlane(lds_tile + (it * W + wave) * 1024));
+  lds_dma_dwordx4(rsrc, d.off[it], __builtin_amdgcn_readfirstlane(lds_tile + (it * W + wave) * 1024));
 }
 
-// The 64 fp32 values v[t*64 .. t*64+63] (zeros past L) into LDS at lds (one
-// piece: lanes 16..63 read past the 256 valid bytes and write zeros).
-__device__ __forceinline__ void dma_vec(const float* v, int t, int L, uint32_t lds, int lane) {
-  lds_dma_dwordx4(buffer_rsrc(v + (int64_t)t * kTile, (int64_t)(L - t * kTile) * 4), 16u * lane,
+template <int W>
+__device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t tok_stride, int t, int L,
+                                         const DmaOffsets<W>& d, uint32_t lds_tile, int wave) {
+#pragma unroll
+  for (int it = 0; it < dma_per_wave<W>(); ++it) dma_row_piece<W>(base, tok_stride, t, L, d, lds_tile, wave, it);
+}
+
+// The 64 fp32 values v[t*64 .. t*64+63] of an n-value vector (zeros past n)
+// into LDS at lds: one 1 KiB piece, whose first 256 bytes are those values.
+__device__ __forceinline__ void dma_vec(const float* v, int t, int n, uint32_t lds, int lane) {
+  lds_dma_dwordx4(buffer_rsrc(v + (int64_t)t * kTile, (int64_t)(n - t * kTile) * 4), 16u * lane,
                   __builtin_amdgcn_readfirstlane(lds));
 }
 
@@ -200,7 +208,7 @@ __device__ __forceinline__ void block_tile(int b, int H, int n_full, int& head, 
 __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ out, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
-    uint16_t* __restrict__ dq, float* __restrict__ delta, int L, int H, float c, float scale, int n_full) {
+    uint16_t* __restrict__ dq, float* __restrict__ stats, int L, int H, int Lp, float c, float scale, int n_full) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStages * kTileBytes];  // K ring, then V ring
   int head, qtile;
   block_tile(blockIdx.x, H, n_full, head, qtile);
@@ -237,8 +245,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
       for (int i = 0; i < 8; ++i) dsum = fmaf((float)dop[ks][i], (float)oop[ks][i], dsum);
   }
   const float dl = pair_sum(dsum);
-  if (valid && g == 0) delta[(int64_t)head * L + row] = dl;
   const float lse2 = valid ? lse[(int64_t)head * L + row] * kLog2e : 0.f;
+  if (g == 0 && row < Lp) {  // statistics for the dk/dv kernel; rows L .. Lp-1 get weight 0 there
+    stats[(int64_t)head * Lp + row] = valid ? -lse2 : -INFINITY;
+    stats[((int64_t)H + head) * Lp + row] = valid ? -dl : 0.f;
+  }
   const Addr a = lds_addresses(lane);
 
   f32x16_t acc[4];
@@ -284,22 +295,127 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- dk, dv
-// Ring slot: Q tile, dO tile, then 1 KiB of lse and 1 KiB of delta.
+// Statistics from the dq kernel (the workspace), fp32 [2][H][Lp]: -lse_i
+// log2(e), then -delta_i, with -inf and 0 in rows L .. Lp-1 so that a query
+// row past L gets weight exp2(-inf) = 0 without a test.
+//
+// Ring slot: Q tile, dO tile, then one 1 KiB DMA piece per statistic (the
+// tile's 64 values in its first 256 bytes).
 constexpr int kSlotBytes = 2 * kTileBytes + 2048;
-
-// dK and dV in one pass over the queries (S computed once per tile): a
-// workgroup of 4 waves, one per SIMD, owning 128 keys.  With one wave per SIMD
-// a wave has 512 registers, enough for both accumulator sets and both operand
-// sets, which only the matrix cores touch, beside the scores, weights and
-// statistics the vector units work on.
+constexpr int kFusedStages = 4;
 constexpr int kFusedWaves = 4;
 constexpr int kFusedRows = 32 * kFusedWaves;
+constexpr int kFusedPieces = 2 * dma_per_wave<kFusedWaves>();  // Q and dO pieces per wave per tile
+constexpr int kAhead = 2;                                       // operand reads this many slots early
+
+// dK and dV in one pass over the queries (S computed once per tile): a
+// workgroup of 4 waves, one per SIMD, owning 128 keys.  One wave per SIMD has
+// 512 registers: the two accumulator sets and the K^T, V^T operands, which
+// only the matrix cores touch, beside the scores and weights of two blocks.
+//
+// With no second wave on the SIMD to fill the matrix cores while the vector
+// units compute weights, the wave does it itself: the queries are taken in
+// 32-row blocks, and the step of block b issues, slot by slot,
+//   S(b+1) = Q K^T, dP'(b+1) = dO V^T - delta   (16 MFMAs; the dP' chain starts
+//                                                 from -delta instead of 0)
+//   dV^T += dO(b-1)^T P(b-1), dK^T += Q(b-1)^T dS(b-1)   (16 MFMAs)
+//   P(b) = exp2(c S - lse log2 e), dS(b) = P dP'  (vector units)
+// none of which depends on another.  Block (t, h) is the h-th half of query
+// tile t.  The step of (t, 0) also starts the DMA of tile t + 2 into the slot
+// of tile t - 2 (last read by the step of (t - 1, 0)), and ends with the one
+// barrier of the tile, after which tile t + 1 (read from the step of (t, 1)
+// on) has landed: each DMA has three steps to arrive.
+struct FusedOps {
+  f32x16_t dka[4], dva[4];
+  bf16x8_t kop[8], vop[8];
+};
+
+// LDS operand of matrix slot k of a step: even k, MFMA k/2 of the next block's
+// S (k/2 even) or dP' (odd), k-step k/4, from its Q or dO rows; odd k, MFMA
+// i = (k-1)/2 = 8 jj + 2 dblk + w of the previous block's dV (w = 0, from dO)
+// or dK (w = 1, from Q), 16-row step 2 qbp + jj, by transposing reads.
+__device__ __forceinline__ bf16x8_t fused_operand(int k, const lds_char* nxt, int qbn, const lds_char* prv,
+                                                  int qbp, const Addr& a) {
+  const int i = k >> 1;
+  if ((k & 1) == 0) return row_operand(nxt + (i & 1) * kTileBytes, qbn, i >> 1, a);
+  return tr_operand(prv + ((i & 1) ? 0 : kTileBytes), (i >> 1) & 3, 2 * qbp + (i >> 3), a);
+}
+
+// The step of one block (slot cur, half qb): next block in slot nxt, half qbn;
+// previous block in slot prv, half qbp (kPrev: there is one).  s_c, dp_c: this
+// block's S and dP'; s_n, dp_n: the next block's, computed here; w*_p: the
+// previous block's packed P and dS (B operands), w*_c: this block's.  Slot k
+// of this block's weights: 2e the exponent of score e, 2e+1 its exponential,
+// 2e+2 dS = P dP', and each bf16 pair packed the slot after its second value;
+// dma(k) issues the step's share of the ring DMA.
+template <bool kPrev, typename Dma>
+__device__ __forceinline__ void fused_step(const lds_char* cur, int qb, const lds_char* nxt, int qbn,
+                                           const lds_char* prv, int qbp, const Addr& a, float c, int g,
+                                           const f32x16_t& s_c, const f32x16_t& dp_c, f32x16_t& s_n,
+                                           f32x16_t& dp_n, const bf16x8_t (&wp_p)[2], const bf16x8_t (&ws_p)[2],
+                                           bf16x8_t (&wp_c)[2], bf16x8_t (&ws_c)[2], FusedOps& fo, const Dma& dma) {
+  float nl[16];
+  f32x16_t dinit;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const f32x4_t l4 = *(const lds_f32x4*)(cur + 2 * kTileBytes + 4 * (32 * qb + 8 * rr + 4 * g));
+    const f32x4_t d4 = *(const lds_f32x4*)(nxt + 2 * kTileBytes + 1024 + 4 * (32 * qbn + 8 * rr + 4 * g));
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      nl[4 * rr + qq] = l4[qq];
+      dinit[4 * rr + qq] = d4[qq];
+    }
+  }
+  s_n = f32x16_t{};
+  dp_n = dinit;
+  bf16x8_t op[32];
+#pragma unroll
+  for (int j = 0; j < kAhead; ++j)
+    if (kPrev || (j & 1) == 0) op[j] = fused_operand(j, nxt, qbn, prv, qbp, a);
+  __builtin_amdgcn_sched_barrier(0);
+  float xa[16], p[16], x[16];
+  uint32_t wpair[8], xpair[8];
+#pragma unroll
+  for (int k = 0; k < 34; ++k) {
+    dma(k);
+    if (k < 32) {
+      const int kk = k + kAhead;
+      if (kk < 32 && (kPrev || (kk & 1) == 0)) op[kk] = fused_operand(kk, nxt, qbn, prv, qbp, a);
+      const int i = k >> 1;
+      if ((k & 1) == 0) {
+        if ((i & 1) == 0) s_n = mfma32(op[k], fo.kop[i >> 1], s_n);
+        else dp_n = mfma32(op[k], fo.vop[i >> 1], dp_n);
+      } else if (kPrev) {
+        const int dblk = (i >> 1) & 3, jj = i >> 3;
+        if ((i & 1) == 0) fo.dva[dblk] = mfma32(op[k], wp_p[jj], fo.dva[dblk]);
+        else fo.dka[dblk] = mfma32(op[k], ws_p[jj], fo.dka[dblk]);
+      }
+    }
+    if (k < 32 && (k & 1) == 0) xa[k >> 1] = fmaf(s_c[k >> 1], c, nl[k >> 1]);
+    if (k < 32 && (k & 1) == 1) p[k >> 1] = __builtin_amdgcn_exp2f(xa[k >> 1]);
+    if (k >= 2 && k <= 32 && (k & 1) == 0) x[(k - 2) >> 1] = p[(k - 2) >> 1] * dp_c[(k - 2) >> 1];
+    if (k >= 4 && k <= 32 && (k & 3) == 0) {
+      const int m = (k - 4) >> 2;
+      wpair[m] = pack_bf16x2(p[2 * m], p[2 * m + 1]);
+    }
+    if (k >= 5 && (k & 3) == 1) {
+      const int m = (k - 5) >> 2;
+      xpair[m] = pack_bf16x2(x[2 * m], x[2 * m + 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    wp_c[h] = __builtin_bit_cast(bf16x8_t, u32x4_t{wpair[4 * h], wpair[4 * h + 1], wpair[4 * h + 2], wpair[4 * h + 3]});
+    ws_c[h] = __builtin_bit_cast(bf16x8_t, u32x4_t{xpair[4 * h], xpair[4 * h + 1], xpair[4 * h + 2], xpair[4 * h + 3]});
+  }
+}
 
 __global__ __launch_bounds__(64 * kFusedWaves, 1) void attention_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    uint16_t* __restrict__ dk_out, uint16_t* __restrict__ dv_out, int L, int H, float c, float scale, int n_full) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kStages * kSlotBytes];
+    const uint16_t* __restrict__ dout, const float* __restrict__ stats, uint16_t* __restrict__ dk_out,
+    uint16_t* __restrict__ dv_out, int L, int H, int Lp, float c, float scale, int n_full) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kFusedStages * kSlotBytes];
   int head, ktile;
   block_tile(blockIdx.x, H, n_full, head, ktile);
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, g = lane >> 5;
@@ -311,103 +427,110 @@ __global__ __launch_bounds__(64 * kFusedWaves, 1) void attention_bwd_dkdv_kernel
   const DmaOffsets<kFusedWaves> dmo = dma_offsets<kFusedWaves>(tok_stride, wave, lane);
   const uint16_t* qh = q + (int64_t)head * kD;
   const uint16_t* doh = dout + (int64_t)head * kD;
-  const float* lseh = lse + (int64_t)head * L;
-  const float* dlh = delta + (int64_t)head * L;
-  auto fill = [&](int t) {
+  const float* nlh = stats + (int64_t)head * Lp;
+  const float* ndh = stats + ((int64_t)H + head) * Lp;
+  // DMA piece j of tile t (clamped to the last tile: refetches keep the count
+  // per step fixed): j = 0..3 Q, 4..7 dO, 8 a statistic -- -lse log2(e) from
+  // even waves, -delta from odd ones (waves 2 and 3 repeat the identical
+  // writes of waves 0 and 1, which keeps the step free of branches).
+  const float* stat_src = (wave & 1) ? ndh : nlh;
+  const uint32_t stat_off = 2 * kTileBytes + 1024 * (wave & 1);
+  auto piece = [&](int t, int j) {
     const int tt = t < n_tiles ? t : n_tiles - 1;
-    const uint32_t s = lds_base + (uint32_t)(t % kStages) * kSlotBytes;
-    dma_rows<kFusedWaves>(qh, tok_stride, tt, L, dmo, s, wave);
-    dma_rows<kFusedWaves>(doh, tok_stride, tt, L, dmo, s + kTileBytes, wave);
-    if (wave == 0) dma_vec(lseh, tt, L, s + 2 * kTileBytes, lane);
-    if (wave == 1) dma_vec(dlh, tt, L, s + 2 * kTileBytes + 1024, lane);
+    const uint32_t s = lds_base + (uint32_t)(t % kFusedStages) * kSlotBytes;
+    if (j < 4) dma_row_piece<kFusedWaves>(qh, tok_stride, tt, L, dmo, s, wave, j);
+    else if (j < 8) dma_row_piece<kFusedWaves>(doh, tok_stride, tt, L, dmo, s + kTileBytes, wave, j - 4);
+    else dma_vec(stat_src, tt, Lp, s + stat_off, lane);
   };
-  fill(0);
-  fill(1);
-  const int key = ktile * kFusedRows + wave * 32 + col;
-  bf16x8_t kop[8], vop[8];
-  load_row_operands(k + (int64_t)head * kD, tok_stride, key, L, g, kop);
-  load_row_operands(v + (int64_t)head * kD, tok_stride, key, L, g, vop);
-  const Addr a = lds_addresses(lane);
-  f32x16_t dka[4], dva[4];
+  const auto slot = [&](int t) { return lds + (t % kFusedStages) * kSlotBytes; };
+  static_assert(kFusedPieces == 8, "the step spreads eight row pieces over its slots");
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dka[i] = dva[i] = f32x16_t{};
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 9; ++j) piece(t, j);
+  const int key = ktile * kFusedRows + wave * 32 + col;
+  FusedOps fo;
+  load_row_operands(k + (int64_t)head * kD, tok_stride, key, L, g, fo.kop);
+  load_row_operands(v + (int64_t)head * kD, tok_stride, key, L, g, fo.vop);
+  const Addr a = lds_addresses(lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fo.dka[i] = fo.dva[i] = f32x16_t{};
   dma_wait();
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    // The accumulators and the K, V operands are read only by the matrix
-    // cores: keep them in the AGPR half.
+
+  // Block (0, 0)'s S and dP'.
+  f32x16_t sa = f32x16_t{}, da, sb, db;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(dka[i]), "+a"(dva[i]));
-    fill(t + 2);
-    const lds_char* slot = lds + (t % kStages) * kSlotBytes;
-    const lds_char* qt = slot;
-    const lds_char* dot = slot + kTileBytes;
-    const lds_char* vec = slot + 2 * kTileBytes;
+  for (int rr = 0; rr < 4; ++rr) {
+    const f32x4_t d4 = *(const lds_f32x4*)(lds + 2 * kTileBytes + 1024 + 4 * (8 * rr + 4 * g));
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+    for (int qq = 0; qq < 4; ++qq) da[4 * rr + qq] = d4[qq];
+  }
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s = mfma32(row_operand(qt, qb, ks, a), kop[ks], s);
-        dp = mfma32(row_operand(dot, qb, ks, a), vop[ks], dp);
-      }
-      // Scores are read by the vector units: keep them in VGPRs.
-      asm volatile("" : "+v"(s), "+v"(dp));
-      float xp[16], xs[16];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r0 = 32 * qb + 8 * rr + 4 * g;
-        const f32x4_t l4 = *(const lds_f32x4*)(vec + 4 * r0);
-        const f32x4_t d4 = *(const lds_f32x4*)(vec + 1024 + 4 * r0);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int e = 4 * rr + qq;
-          const float p = t * kTile + r0 + qq < L ? __builtin_amdgcn_exp2f(fmaf(s[e], c, -l4[qq] * kLog2e)) : 0.f;
-          xp[e] = p;
-          xs[e] = p * (dp[e] - d4[qq]);
-        }
-      }
-      bf16x8_t wp[2], wsv[2];
-      pack_operands(xp, wp);
-      pack_operands(xs, wsv);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int dblk = 0; dblk < 4; ++dblk) {
-          dva[dblk] = mfma32(tr_operand(dot, dblk, 2 * qb + jj, a), wp[jj], dva[dblk]);
-          dka[dblk] = mfma32(tr_operand(qt, dblk, 2 * qb + jj, a), wsv[jj], dka[dblk]);
-        }
-    }
-    if (wave < 2) dma_wait_all_but<2 * dma_per_wave<kFusedWaves>() + 1>();
-    else dma_wait_all_but<2 * dma_per_wave<kFusedWaves>()>();
+  for (int ks = 0; ks < 8; ++ks) {
+    sa = mfma32(row_operand(lds, 0, ks, a), fo.kop[ks], sa);
+    da = mfma32(row_operand(lds + kTileBytes, 0, ks, a), fo.vop[ks], da);
+  }
+  asm volatile("" : "+v"(sa), "+v"(da));
+  // Block (t, 0) runs on set a (S, dP') and produces pa; block (t, 1) on set b, producing pb.
+  bf16x8_t wpa[2], wsa[2], wpb[2], wsb[2];
+  const auto no_dma = [](int) {};
+  const auto wait_and_sync = [&]() {
+    dma_wait_all_but<kFusedPieces + 1>();  // tile t + 1 landed; tile t + 2 may be in flight
     __syncthreads();
+  };
+  {
+    const auto dma = [&](int kslot) {
+      if ((kslot & 3) == 1 && kslot < 32) piece(2, kslot >> 2);
+      if (kslot == 3) piece(2, 8);
+    };
+    fused_step<false>(slot(0), 0, slot(0), 1, slot(0), 0, a, c, g, sa, da, sb, db, wpb, wsb, wpa, wsa, fo, dma);
+    wait_and_sync();
+  }
+  // The last trip's second step, block (n_tiles, 0), finishes dV and dK of the
+  // last block; its own scores come from a stale (loaded) slot and are never
+  // used, like those of the next block in the first step of that trip.
+  for (int t = 0; t < n_tiles; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(fo.dka[i]), "+a"(fo.dva[i]));
+    fused_step<true>(slot(t), 1, slot(t + 1), 0, slot(t), 0, a, c, g, sb, db, sa, da, wpa, wsa, wpb, wsb, fo,
+                     no_dma);
+    const auto dma = [&](int kslot) {
+      if ((kslot & 3) == 1 && kslot < 32) piece(t + 3, kslot >> 2);
+      if (kslot == 3) piece(t + 3, 8);
+    };
+    fused_step<true>(slot(t + 1), 0, slot(t + 1), 1, slot(t), 1, a, c, g, sa, da, sb, db, wpb, wsb, wpa, wsa, fo,
+                     dma);
+    wait_and_sync();
   }
   dma_wait();
   if (key < L) {
-    store_transposed(dk_out + (int64_t)key * tok_stride + (int64_t)head * kD, dka, scale, g);
-    store_transposed(dv_out + (int64_t)key * tok_stride + (int64_t)head * kD, dva, 1.0f, g);
+    store_transposed(dk_out + (int64_t)key * tok_stride + (int64_t)head * kD, fo.dka, scale, g);
+    store_transposed(dv_out + (int64_t)key * tok_stride + (int64_t)head * kD, fo.dva, 1.0f, g);
   }
 }
 
 }  // namespace
 
 int64_t backward_grid_blocks(int64_t L, int32_t H) { return ((L + kRows - 1) / kRows) * (int64_t)H; }
+int64_t backward_workspace_bytes(int64_t L, int32_t H) { return 2 * (int64_t)H * ((L + kTile - 1) / kTile * kTile) * 4; }
 int backward_block_threads() { return kThreads; }
 
 hipError_t launch_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* out, const uint16_t* dout, const float* lse,
-                                     uint16_t* dq, uint16_t* dk, uint16_t* dv, float* delta, int64_t L,
+                                     uint16_t* dq, uint16_t* dk, uint16_t* dv, float* stats, int64_t L,
                                      int32_t H, float scale, hipStream_t stream) {
   const dim3 grid((unsigned)backward_grid_blocks(L, H)), block(kThreads);
   const int n_full = (int)(L / kRows);
+  const int Lp = (int)((L + kTile - 1) / kTile * kTile);
   const float c = scale * kLog2e;
-  hipLaunchKernelGGL(attention_bwd_dq_kernel, grid, block, 0, stream, q, k, v, out, dout, lse, dq, delta, (int)L,
-                     (int)H, c, scale, n_full);
+  hipLaunchKernelGGL(attention_bwd_dq_kernel, grid, block, 0, stream, q, k, v, out, dout, lse, dq, stats, (int)L,
+                     (int)H, Lp, c, scale, n_full);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 fgrid((unsigned)(((L + kFusedRows - 1) / kFusedRows) * (int64_t)H));
-  hipLaunchKernelGGL(attention_bwd_dkdv_kernel, fgrid, dim3(64 * kFusedWaves), 0, stream, q, k, v, dout, lse, delta,
-                     dk, dv, (int)L, (int)H, c, scale, (int)(L / kFusedRows));
+  hipLaunchKernelGGL(attention_bwd_dkdv_kernel, fgrid, dim3(64 * kFusedWaves), 0, stream, q, k, v, dout, stats,
+                     dk, dv, (int)L, (int)H, Lp, c, scale, (int)(L / kFusedRows));
   return hipGetLastError();
 }
 

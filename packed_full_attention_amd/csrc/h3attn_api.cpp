@@ -216,7 +216,7 @@ int64_t h3attn_attention_backward_workspace_bytes(int64_t L, int32_t H) {
   uint64_t bytes = 0;
   if (check_shape(L, H, &bytes) != H3A_OK) return -1;
   ok();
-  return L * (int64_t)H * 4;
+  return h3attn::backward_workspace_bytes(L, H);
 }
 
 int h3attn_attention_backward(const void* q, const void* k, const void* v, const void* out,
@@ -231,10 +231,10 @@ int h3attn_attention_backward(const void* q, const void* k, const void* v, const
     if (!aligned(p, 16)) return fail(H3A_EINVAL, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned%s");
   if (!aligned(lse, 4) || !aligned(workspace, 4)) return fail(H3A_EINVAL, "lse and workspace must be 4-byte aligned%s");
   if (!(isfinite(scale) && scale > 0.0f)) return fail(H3A_EINVAL, "scale must be finite and > 0%s");
-  const uint64_t vec = (uint64_t)L * H * 4;
+  const uint64_t vec = (uint64_t)L * H * 4, ws = (uint64_t)h3attn::backward_workspace_bytes(L, H);
   // Written ranges: dq, dk, dv, workspace; none may meet another or any input.
   const void* wr[4] = {dq, dk, dv, workspace};
-  const uint64_t wn[4] = {bytes, bytes, bytes, vec};
+  const uint64_t wn[4] = {bytes, bytes, bytes, ws};
   const void* in[6] = {q, k, v, out, dout, lse};
   const uint64_t inn[6] = {bytes, bytes, bytes, bytes, bytes, vec};
   for (int i = 0; i < 4; ++i) {

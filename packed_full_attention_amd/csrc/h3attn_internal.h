@@ -36,14 +36,16 @@ hipError_t launch_attention_forward_qprologue(const uint16_t* q_raw, const uint1
                                               uint16_t* out, const float* gamma_q, const float* rope_cs,
                                               int64_t L, int32_t H, float q_scale, hipStream_t stream);
 
-// Enqueue the attention backward (three kernels, in this order): dq and the
-// per-row delta = <dout, out> (fp32 [H][L], written), then dv, then dk.
-// q, k are the prologue outputs, lse the forward's [H][L] log-sum-exp.
+// Enqueue the attention backward (two kernels, in this order): dq and the
+// per-row statistics -lse log2(e) and -delta = -<dout, out> (stats, fp32
+// [2][H][Lp], Lp = L rounded up to 64; written), then dk and dv.  q, k are
+// the prologue outputs, lse the forward's [H][L] log-sum-exp.
 hipError_t launch_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* out, const uint16_t* dout, const float* lse,
-                                     uint16_t* dq, uint16_t* dk, uint16_t* dv, float* delta, int64_t L,
+                                     uint16_t* dq, uint16_t* dk, uint16_t* dv, float* stats, int64_t L,
                                      int32_t H, float scale, hipStream_t stream);
 int64_t backward_grid_blocks(int64_t L, int32_t H);
+int64_t backward_workspace_bytes(int64_t L, int32_t H);
 int backward_block_threads();
 
 // Backward of the prologue (in place on dq, dk) and the gamma gradients;
