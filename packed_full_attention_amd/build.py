@@ -31,6 +31,11 @@ DEVICE_FLAGS = [
     "-std=c++17",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-instruction accumulators in VGPRs even in kernels that use more
+    # than 256 registers (the one-wave-per-SIMD dK/dV kernel): its scores are
+    # read by vector instructions, and the AGPR half then holds the operands
+    # that only the matrix cores read.  The other kernels compile to the same code.
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
 ]
 HOST_FLAGS = ["-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter"]
 

@@ -56,7 +56,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;                       // rows a workgroup owns
 constexpr int kTile = 64;                                // rows per streamed tile
 constexpr int kTileBytes = kTile * kD * 2;               // 16 KiB
-constexpr int kStages = 3;
 constexpr float kLog2e = 1.4426950408889634f;
 // ---------------------------------------------------------------- tile DMA
 // A 64-row tile of a [L][H][128] tensor: 16 pieces of 1 KiB, wave w writing
@@ -205,11 +204,101 @@ __device__ __forceinline__ void block_tile(int b, int H, int n_full, int& head, 
 }
 
 // ---------------------------------------------------------------- dq (+ delta)
+// Software-pipelined over 32-key blocks, like the dk/dv kernel below but at
+// two waves per SIMD: block (t, kb) is the kb-th half of key tile t, and the
+// step of a block issues, over 24 matrix slots,
+//   S^T = K Q^T and dP^T = V dO^T of the next block   (16 MFMAs)
+//   dQ^T += K^T dS^T of the previous block            (8 MFMAs)
+// and this block's weights, P = exp2(c S - lse log2 e), dS = P (dP - delta).
+// Slot k with k % 3 == 2 holds dQ MFMA k / 3 (= 4 jj + dblk); every other
+// slot holds MFMA n = 2 (k / 3) + k % 3 of the next block, S for even n and dP
+// for odd n, k-step n / 2.  Element e of this block's weights starts at slot
+// 3e / 2 (exponent), then its exponential, then dS, and each bf16 pair is
+// packed the slot after its second dS.  K and V come through rings of four
+// 64-key tiles (128 KiB); the step of (t, 0) starts the DMA of tile t + 2 into
+// the slot of tile t - 2 and ends with the tile's one barrier.
+//
+// The weights are computed halved, P/2 = exp2(c S - lse log2 e - 1) with the
+// exponential's output clamped to [0, 1] (a free instruction modifier), and dQ
+// is scaled by 2 scale at the end: every true weight is at most 1 (up to the
+// forward's rounding of lse), so the clamp never touches one, while keys past
+// L (in the last tile only), whose K and V rows read as zeros, get a finite
+// weight whatever the row's log-sum-exp -- their dS then adds K-row zeros to
+// dQ with no test.
+constexpr int kDqStages = 4;
+constexpr int kDqPieces = 2 * dma_per_wave<kWaves>();  // K and V pieces per wave per tile
+
+__device__ __forceinline__ bf16x8_t dq_operand(int k, const lds_char* nk, const lds_char* nv, int kbn,
+                                               const lds_char* pk, int kbp, const Addr& a) {
+  if (k % 3 == 2) {
+    const int i = k / 3;
+    return tr_operand(pk, i & 3, 2 * kbp + (i >> 2), a);
+  }
+  const int n = 2 * (k / 3) + k % 3;
+  return row_operand((n & 1) ? nv : nk, kbn, n >> 1, a);
+}
+
+constexpr int dq_slot(int e) { return (3 * e) / 2; }
+
+// One step: next block in K/V slots nk, nv (half kbn), previous block in K
+// slot pk (half kbp; kPrev: there is one).  s_c, dp_c: this block's S^T and
+// dP^T; s_n, dp_n: the next block's; ds_p: the previous block's dS^T / 2
+// operand, ds_c: this block's.  nl = -lse log2(e) - 1, dl = delta of the
+// lane's query row.
+template <bool kPrev, typename Dma>
+__device__ __forceinline__ void dq_step(const lds_char* nk, const lds_char* nv, int kbn, const lds_char* pk, int kbp,
+                                        const Addr& a, float c, float nl, float dl, const f32x16_t& s_c,
+                                        const f32x16_t& dp_c, f32x16_t& s_n, f32x16_t& dp_n,
+                                        const bf16x8_t (&ds_p)[2], bf16x8_t (&ds_c)[2], f32x16_t (&acc)[4],
+                                        const bf16x8_t (&qop)[8], const bf16x8_t (&dop)[8], const Dma& dma) {
+  constexpr int kAheadDq = 2;
+  s_n = f32x16_t{};
+  dp_n = f32x16_t{};
+  bf16x8_t op[24];
+#pragma unroll
+  for (int j = 0; j < kAheadDq; ++j)
+    if (kPrev || j % 3 != 2) op[j] = dq_operand(j, nk, nv, kbn, pk, kbp, a);
+  __builtin_amdgcn_sched_barrier(0);
+  float xa[16], p[16], x[16];
+  uint32_t pair[8];
+#pragma unroll
+  for (int k = 0; k < dq_slot(15) + 4; ++k) {
+    dma(k);
+    if (k < 24) {
+      const int kk = k + kAheadDq;
+      if (kk < 24 && (kPrev || kk % 3 != 2)) op[kk] = dq_operand(kk, nk, nv, kbn, pk, kbp, a);
+      if (k % 3 == 2) {
+        if (kPrev) {
+          const int i = k / 3;
+          acc[i & 3] = mfma32(op[k], ds_p[i >> 2], acc[i & 3]);
+        }
+      } else {
+        const int n = 2 * (k / 3) + k % 3;
+        if (n & 1) dp_n = mfma32(op[k], dop[n >> 1], dp_n);
+        else s_n = mfma32(op[k], qop[n >> 1], s_n);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if (k == dq_slot(e)) xa[e] = fmaf(s_c[e], c, nl);
+      if (k == dq_slot(e) + 1) p[e] = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(xa[e]), 0.f, 1.f);
+      if (k == dq_slot(e) + 2) x[e] = p[e] * (dp_c[e] - dl);
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      if (k == dq_slot(2 * m + 1) + 3) pair[m] = pack_bf16x2(x[2 * m], x[2 * m + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    ds_c[h] = __builtin_bit_cast(bf16x8_t, u32x4_t{pair[4 * h], pair[4 * h + 1], pair[4 * h + 2], pair[4 * h + 3]});
+}
+
 __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ out, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     uint16_t* __restrict__ dq, float* __restrict__ stats, int L, int H, int Lp, float c, float scale, int n_full) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStages * kTileBytes];  // K ring, then V ring
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kDqStages * kTileBytes];  // K ring, then V ring
   int head, qtile;
   block_tile(blockIdx.x, H, n_full, head, qtile);
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, g = lane >> 5;
@@ -221,14 +310,23 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
   const DmaOffsets<kWaves> dmo = dma_offsets<kWaves>(tok_stride, wave, lane);
   const uint16_t* kh = k + (int64_t)head * kD;
   const uint16_t* vh = v + (int64_t)head * kD;
-  auto fill = [&](int t) {
-    const int tt = t < n_tiles ? t : n_tiles - 1;  // refetch past the end keeps the count fixed
-    const uint32_t s = (uint32_t)(t % kStages) * kTileBytes;
-    dma_rows(kh, tok_stride, tt, L, dmo, lds_base + s, wave);
-    dma_rows(vh, tok_stride, tt, L, dmo, lds_base + kStages * kTileBytes + s, wave);
+  // DMA piece j of tile t (clamped to the last tile: refetches keep the count
+  // per step fixed): the first half K, the second V.
+  constexpr int kHalf = kDqPieces / 2;
+  auto piece = [&](int t, int j) {
+    const int tt = t < n_tiles ? t : n_tiles - 1;
+    const uint32_t s = lds_base + (uint32_t)(t % kDqStages) * kTileBytes;
+    if (j < kHalf) dma_row_piece<kWaves>(kh, tok_stride, tt, L, dmo, s, wave, j);
+    else dma_row_piece<kWaves>(vh, tok_stride, tt, L, dmo, s + kDqStages * kTileBytes, wave, j - kHalf);
   };
-  fill(0);
-  fill(1);
+  const auto kslot = [&](int t) { return lds + (t % kDqStages) * kTileBytes; };
+  const auto vslot = [&](int t) { return lds + (kDqStages + t % kDqStages) * kTileBytes; };
+  constexpr int kEvery = 24 / kDqPieces;  // the step issues one piece every kEvery slots
+  static_assert(kEvery * kDqPieces == 24, "the pieces spread evenly over the 24 slots");
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < kDqPieces; ++j) piece(t, j);
 
   const int row = qtile * kRows + wave * 32 + col;
   const bool valid = row < L;
@@ -250,6 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
     stats[(int64_t)head * Lp + row] = valid ? -lse2 : -INFINITY;
     stats[((int64_t)H + head) * Lp + row] = valid ? -dl : 0.f;
   }
+  const float nl = -lse2 - 1.0f;  // halved weights (see above)
   const Addr a = lds_addresses(lane);
 
   f32x16_t acc[4];
@@ -257,41 +356,44 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
   for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
   dma_wait();
   __syncthreads();
+
+  // Block (0, 0)'s scores.
+  f32x16_t sa = f32x16_t{}, da = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    sa = mfma32(row_operand(kslot(0), 0, ks, a), qop[ks], sa);
+    da = mfma32(row_operand(vslot(0), 0, ks, a), dop[ks], da);
+  }
+  // The last trip's second step, block (n_tiles, 0), finishes dQ of the last
+  // block; its own scores come from a stale (loaded) slot and are never used.
+  f32x16_t sb, db;
+  bf16x8_t dsa[2], dsb[2];
+  const auto no_dma = [](int) {};
+  {
+    const auto dma = [&](int ks) {
+      if (ks % kEvery == 1 && ks < 24) piece(2, ks / kEvery);
+    };
+    dq_step<false>(kslot(0), vslot(0), 1, kslot(0), 0, a, c, nl, dl, sa, da, sb, db, dsb, dsa, acc, qop, dop, dma);
+    dma_wait_all_but<kDqPieces>();  // tile 1 landed; tile 2 may be in flight
+    __syncthreads();
+  }
   for (int t = 0; t < n_tiles; ++t) {
-    fill(t + 2);  // into the slot of tile t-1, which every wave finished before the last barrier
-    const lds_char* kt = lds + (t % kStages) * kTileBytes;
-    const lds_char* vt = lds + kStages * kTileBytes + (t % kStages) * kTileBytes;
-    // One 32-key block at a time (keeps two score blocks' registers free).
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s = mfma32(row_operand(kt, kb, ks, a), qop[ks], s);
-        dp = mfma32(row_operand(vt, kb, ks, a), dop[ks], dp);
-      }
-      // dS^T = P^T (dP^T - delta); slot 4 rr + qq is key 32 kb + 8 rr + 4 g + qq.
-      float x[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = t * kTile + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-        const float p = key < L ? __builtin_amdgcn_exp2f(fmaf(s[e], c, -lse2)) : 0.f;
-        x[e] = p * (dp[e] - dl);
-      }
-      bf16x8_t ds[2];
-      pack_operands(x, ds);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int dblk = 0; dblk < 4; ++dblk)
-          acc[dblk] = mfma32(tr_operand(kt, dblk, 2 * kb + jj, a), ds[jj], acc[dblk]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    dma_wait_all_but<2 * dma_per_wave<kWaves>()>();  // tile t+1 landed (tile t+2 may be in flight)
+    dq_step<true>(kslot(t + 1), vslot(t + 1), 0, kslot(t), 0, a, c, nl, dl, sb, db, sa, da, dsa, dsb, acc, qop, dop,
+                  no_dma);
+    const auto dma = [&](int ks) {
+      if (ks % kEvery == 1 && ks < 24) piece(t + 3, ks / kEvery);
+    };
+    dq_step<true>(kslot(t + 1), vslot(t + 1), 1, kslot(t), 1, a, c, nl, dl, sa, da, sb, db, dsb, dsa, acc, qop, dop,
+                  dma);
+    dma_wait_all_but<kDqPieces>();
     __syncthreads();
   }
   dma_wait();
-  if (valid) store_transposed(dq + (int64_t)row * tok_stride + (int64_t)head * kD, acc, scale, g);
+  // The row's 64-bit offset again (an opaque copy of row keeps the compiler
+  // from holding the one computed for the loads through the loop).
+  int orow = row;
+  asm volatile("" : "+v"(orow));
+  if (valid) store_transposed(dq + (int64_t)orow * tok_stride + (int64_t)head * kD, acc, 2.0f * scale, g);
 }
 
 // ---------------------------------------------------------------- dk, dv
@@ -310,8 +412,10 @@ constexpr int kAhead = 2;                                       // operand reads
 
 // dK and dV in one pass over the queries (S computed once per tile): a
 // workgroup of 4 waves, one per SIMD, owning 128 keys.  One wave per SIMD has
-// 512 registers: the two accumulator sets and the K^T, V^T operands, which
-// only the matrix cores touch, beside the scores and weights of two blocks.
+// 512 registers: the two accumulator sets and the scores and weights of two
+// blocks in VGPRs, the K^T, V^T operands (read only by the matrix cores) in
+// AGPRs; the build keeps matrix accumulators in VGPRs, so the vector units
+// read the scores where the matrix cores leave them.
 //
 // With no second wave on the SIMD to fill the matrix cores while the vector
 // units compute weights, the wave does it itself: the queries are taken in
@@ -491,8 +595,6 @@ __global__ __launch_bounds__(64 * kFusedWaves, 1) void attention_bwd_dkdv_kernel
   // last block; its own scores come from a stale (loaded) slot and are never
   // used, like those of the next block in the first step of that trip.
   for (int t = 0; t < n_tiles; ++t) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(fo.dka[i]), "+a"(fo.dva[i]));
     fused_step<true>(slot(t), 1, slot(t + 1), 0, slot(t), 0, a, c, g, sb, db, sa, da, wpa, wsa, wpb, wsb, fo,
                      no_dma);
     const auto dma = [&](int kslot) {

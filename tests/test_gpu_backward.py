@@ -120,6 +120,28 @@ def test_attention_backward_ragged_lengths(L):
     _compare_attention(f"L={L}", q, k, v, (dq, dk, dv), do_bits)
 
 
+def test_attention_backward_very_negative_scores():
+    """Query rows whose every score is far below zero (log-sum-exp near -100),
+    with keys past L in the last tile (L = 200): the weight those absent keys
+    would get, exp(-lse), overflows fp32, so the dq kernel must keep it out of
+    dQ.  The keys share a direction u, but each also has a random part as large
+    (nearly equal keys would make dQ = scale sum_j dS_j k_j cancel down to the
+    bf16 rounding of dS for any kernel)."""
+    L, H = 200, 1
+    rng = np.random.default_rng(77)
+    u = 1.0 + 0.05 * rng.standard_normal(128)
+    k_f = (u[None, :] + rng.standard_normal((L, 128)))[:, None, :]
+    q_f = rng.standard_normal((L, H, 128))
+    q_f[::7] = -12.0 * u  # every 7th query row: scores between about -165 and -100
+    q = dev_bf16(wl.bf16_bits(q_f.astype(np.float32)))
+    k = dev_bf16(wl.bf16_bits(k_f.astype(np.float32)))
+    v = dev_bf16(_bf16_normal((L, H, 128), 78))
+    dq, dk, dv, do_bits = _attention_case(q, k, v, 79)
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    _compare_attention("very negative scores", q, k, v, (dq, dk, dv), do_bits)
+
+
 def test_attention_backward_long_heads(inputs):
     """L = 16500, H = 56, the whole grid on the GPU; two heads compared in full."""
     inp = inputs(3)
