@@ -291,26 +291,39 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_bwd_kernel(
   partial[(int64_t)blockIdx.x * 2 * kHeadDim + c] = acc;
 }
 
-// out[j][c] = sum over rows j*256 .. j*256+255 (< n) of in[row][c], c < 256,
-// rows added in increasing order.
-constexpr int kReduceRows = 256;
+// out[j][c] = sum over rows j*32 .. j*32+31 (< n) of in[row][c], c < 256,
+// rows added in increasing order.  All of a thread's loads are issued before
+// the first add (a dependent chain of loads would leave the kernel waiting on
+// memory latency row after row).
+constexpr int kReduceRows = 32;
 
 __global__ __launch_bounds__(2 * kHeadDim) void gamma_reduce_kernel(const float* __restrict__ in,
                                                                     float* __restrict__ out, int64_t n) {
   const int c = threadIdx.x;
   const int64_t r0 = (int64_t)blockIdx.x * kReduceRows;
-  const int64_t r1 = r0 + kReduceRows < n ? r0 + kReduceRows : n;
-  float acc = 0.f;
-  for (int64_t r = r0; r < r1; ++r) acc += in[r * 2 * kHeadDim + c];
+  float x[kReduceRows];
+#pragma unroll
+  for (int i = 0; i < kReduceRows; ++i) x[i] = r0 + i < n ? in[(r0 + i) * 2 * kHeadDim + c] : 0.f;
+  float acc = x[0];
+#pragma unroll
+  for (int i = 1; i < kReduceRows; ++i) acc += x[i];
   out[(int64_t)blockIdx.x * 2 * kHeadDim + c] = acc;
 }
 
-// The last stage: 256 sums -> dgamma_q (c < 128), dgamma_k.
+// The last stage: the n group sums, in order -> dgamma_q (c < 128), dgamma_k;
+// 16 loads in flight ahead of the adds.
 __global__ __launch_bounds__(2 * kHeadDim) void gamma_final_kernel(const float* __restrict__ in, float* __restrict__ dgq,
                                                                    float* __restrict__ dgk, int64_t n) {
   const int c = threadIdx.x;
   float acc = 0.f;
-  for (int64_t r = 0; r < n; ++r) acc += in[r * 2 * kHeadDim + c];
+  for (int64_t r0 = 0; r0 < n; r0 += 16) {
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = r0 + i < n ? in[(r0 + i) * 2 * kHeadDim + c] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (r0 + i < n) acc += x[i];
+  }
   if (c < kHeadDim) dgq[c] = acc;
   else dgk[c - kHeadDim] = acc;
 }
