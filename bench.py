@@ -145,8 +145,8 @@ def main() -> int:
     import numpy as np
     import torch
     from packed_full_attention_amd import (h3attn_attention_backward, h3attn_forward, h3attn_forward_log2,
-                                           h3attn_forward_log2_qprologue, h3attn_forward_lse,
-                                           h3attn_k_prologue_table, h3attn_qk_prologue, h3attn_qk_prologue_backward,
+                                           h3attn_forward_log2_lse, h3attn_forward_log2_qprologue,
+                                           h3attn_k_prologue_table, h3attn_qk_prologue, h3attn_qk_prologue_backward_scaled,
                                            h3attn_qk_prologue_scaled, h3attn_v_transpose, load_library)
     from packed_full_attention_amd import workloads as wl
 
@@ -237,11 +237,12 @@ def main() -> int:
     ms_step, (t_kpro, t_vt, t_att), wall_ms = timed(fused, K, W)
     del qs, ks
 
-    # Training pieces, timed separately (not part of `value`): the forward with
-    # log-sum-exp, the attention backward and the prologue backward, on the
+    # Training pieces, timed separately (not part of `value`), in the scale-folded
+    # layout: the log2 forward with log-sum-exp, the attention backward on
+    # q' = c q at scale ln 2, and the scaled prologue backward, on the scaled
     # prologue's outputs of this workload and a seeded dO.
     qp, kp = q.clone(), k.clone()
-    h3attn_qk_prologue(qp, kp, gq, gk, pos)
+    h3attn_qk_prologue_scaled(qp, kp, gq, gk, pos, q_scale)
     gen = torch.Generator(device=dev).manual_seed(1000 + w.index)
     dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
     out2, lse = torch.empty_like(q), torch.empty(H, L, dtype=torch.float32, device=dev)
@@ -250,9 +251,9 @@ def main() -> int:
     pws = torch.empty(int(load_library().h3attn_qk_prologue_backward_workspace_bytes(L, H)), dtype=torch.uint8,
                       device=dev)
     dgq, dgk = torch.empty(128, device=dev), torch.empty(128, device=dev)
-    train = [lambda i: h3attn_forward_lse(qp, kp, v, out2, lse, scale=scale),
-             lambda i: h3attn_attention_backward(qp, kp, v, out2, dout, lse, dq, dk, dv, ws, scale=scale),
-             lambda i: h3attn_qk_prologue_backward(q, k, gq, gk, pos, dq, dk, dgq, dgk, pws)]
+    train = [lambda i: h3attn_forward_log2_lse(qp, kp, vt, out2, lse),
+             lambda i: h3attn_attention_backward(qp, kp, v, out2, dout, lse, dq, dk, dv, ws, scale=math.log(2.0)),
+             lambda i: h3attn_qk_prologue_backward_scaled(q, k, gq, gk, pos, dq, dk, q_scale, dgq, dgk, pws)]
     for i in range(W):
         for f in train:
             f(i)
@@ -323,7 +324,9 @@ def main() -> int:
                        "attention_ms": round(plain_att, 4),
                        "attention_tflops": round(flops / (plain_att * 1e-3) / 1e12, 2),
                        "prologue_us": round(plain_pro * 1e3, 2)},
-        "backward": {"forward_lse_ms": round(t_fl, 4),
+        "backward": {"entry_points": "h3attn_forward_log2_lse + h3attn_attention_backward (q' = c q, scale ln 2) + "
+                                     "h3attn_qk_prologue_backward_scaled",
+                     "forward_lse_ms": round(t_fl, 4),
                      "attention_backward_ms": round(t_bwd, 4),
                      "attention_backward_tflops": round(bwd_flops / (t_bwd * 1e-3) / 1e12, 2),
                      "attention_backward_frac": round(bwd_flops / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

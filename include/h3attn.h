@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 4
+#define H3ATTN_ABI_VERSION 5
 #define H3ATTN_HEAD_DIM 128
 
 /* Status codes. */
@@ -210,6 +210,26 @@ int h3attn_forward_log2_qprologue(const void* q, const void* k, const void* vt, 
  *   bytes.  The gamma sums are added in a fixed order (deterministic).
  *
  * The *_workspace_bytes calls return -1 for an (L, H) the others reject.
+ *
+ * The training step in the scale-folded layout (c = fp32(scale * log2(e))):
+ *   h3attn_qk_prologue_scaled(q, k, ..., c, s)            q' = c * prologue(q)
+ *   h3attn_v_transpose(v, vt, L, H, s)
+ *   h3attn_forward_log2_lse(q', k, vt, out, lse, L, H, s)
+ *   h3attn_attention_backward(q', k, v, out, dout, lse, dq', dk, dv, ws, L, H, ln 2, s)
+ *   h3attn_qk_prologue_backward_scaled(q, k, ..., dq', dk, ..., c, s)
+ * gives the gradients of the plain path: ln 2 * <q', k> is the scaled score,
+ * so the attention backward at scale ln 2 returns dk, dv and the gradient with
+ * respect to q', which the scaled prologue backward carries back to the raw q.
+ *
+ * h3attn_forward_log2_lse: h3attn_forward_log2, and in addition
+ *   lse[h*L + i] = ln( sum_j 2^<q[i,h,:], k[j,h,:]> )  (= ln sum_j exp(scale <q_raw', k>)
+ *   for q = c * q_raw'), fp32 [H][L], as for h3attn_forward_lse.
+ *
+ * h3attn_qk_prologue_backward_scaled: h3attn_qk_prologue_backward for the
+ *   prologue that h3attn_qk_prologue_scaled computed with this q_scale (finite,
+ *   > 0): dq holds the gradient with respect to Q's scaled output, Q's weights
+ *   are gamma_q * q_scale (fp32) and dgamma_q is q_scale * sum(dy x r).  With
+ *   q_scale = 1 it is h3attn_qk_prologue_backward, bit for bit.
  */
 int h3attn_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse, int64_t L,
                        int32_t H, float scale, hipStream_t stream);
@@ -217,11 +237,17 @@ int64_t h3attn_attention_backward_workspace_bytes(int64_t L, int32_t H);
 int h3attn_attention_backward(const void* q, const void* k, const void* v, const void* out,
                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
                               void* workspace, int64_t L, int32_t H, float scale, hipStream_t stream);
+int h3attn_forward_log2_lse(const void* q, const void* k, const void* vt, void* out, float* lse, int64_t L,
+                            int32_t H, hipStream_t stream);
 int64_t h3attn_qk_prologue_backward_workspace_bytes(int64_t L, int32_t H);
 int h3attn_qk_prologue_backward(const void* q, const void* k, const float* gamma_q, const float* gamma_k,
                                 const int32_t* pos_thw, void* dq, void* dk, float* dgamma_q,
                                 float* dgamma_k, void* workspace, int64_t L, int32_t H,
                                 hipStream_t stream);
+int h3attn_qk_prologue_backward_scaled(const void* q, const void* k, const float* gamma_q,
+                                       const float* gamma_k, const int32_t* pos_thw, void* dq, void* dk,
+                                       float* dgamma_q, float* dgamma_k, void* workspace, int64_t L,
+                                       int32_t H, float q_scale, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* h3attn_strerror(int status);

@@ -22,6 +22,7 @@ EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward", "h3attn_qk_prologue_
                     "h3attn_attention_backward_workspace_bytes", "h3attn_attention_backward",
                     "h3attn_qk_prologue_backward_workspace_bytes", "h3attn_qk_prologue_backward",
                     "h3attn_rope_table_bytes", "h3attn_k_prologue_table", "h3attn_forward_log2_qprologue",
+                    "h3attn_forward_log2_lse", "h3attn_qk_prologue_backward_scaled",
                     "h3attn_strerror", "h3attn_last_error", "h3attn_abi_version")
 
 _lock = threading.Lock()
@@ -73,6 +74,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.h3attn_k_prologue_table.restype = ctypes.c_int
         lib.h3attn_forward_log2_qprologue.argtypes = [vp] * 6 + [i64, i32, ctypes.c_float, vp]
         lib.h3attn_forward_log2_qprologue.restype = ctypes.c_int
+        lib.h3attn_forward_log2_lse.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp]
+        lib.h3attn_forward_log2_lse.restype = ctypes.c_int
+        lib.h3attn_qk_prologue_backward_scaled.argtypes = [vp] * 10 + [i64, i32, ctypes.c_float, vp]
+        lib.h3attn_qk_prologue_backward_scaled.restype = ctypes.c_int
         lib.h3attn_strerror.argtypes = [ctypes.c_int]
         lib.h3attn_strerror.restype = ctypes.c_char_p
         lib.h3attn_last_error.argtypes = []
@@ -243,25 +248,40 @@ def h3attn_forward_log2_qprologue(q, k, vt, gamma_q, rope_cs, q_scale: float, ou
     return out
 
 
-def h3attn_forward_lse(q, k, v, out=None, lse=None, scale: Optional[float] = None):
-    """h3attn_forward that also returns each row's natural log-sum-exp, fp32 [H, L]:
-    returns (out, lse)."""
+def _forward_lse(fn, q, k, v, out, lse, scale):
     import torch
     L, H = _lh(q)
     dev = q.device
-    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(name, t, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    _check_tensor("q", q, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    _check_tensor("k", k, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    if scale is None:
+        _check_tensor("vt", v, torch.bfloat16, (H, HEAD_DIM, padded_length(L)), dev)
+    else:
+        _check_tensor("v", v, torch.bfloat16, (L, H, HEAD_DIM), dev)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(H, L, dtype=torch.float32, device=dev) if lse is None else lse
     _check_tensor("out", out, torch.bfloat16, (L, H, HEAD_DIM), dev)
     _check_tensor("lse", lse, torch.float32, (H, L), dev)
     lib = load_library()
     with torch.cuda.device(dev):
-        st = lib.h3attn_forward_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), L, H,
-                                    scale, torch.cuda.current_stream(dev).cuda_stream)
-    _raise_on(lib, "h3attn_forward_lse", st)
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), L, H)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.h3attn_forward_log2_lse(*args, stream) if scale is None else lib.h3attn_forward_lse(*args, scale, stream)
+    _raise_on(lib, fn, st)
     return out, lse
+
+
+def h3attn_forward_lse(q, k, v, out=None, lse=None, scale: Optional[float] = None):
+    """h3attn_forward that also returns each row's natural log-sum-exp, fp32 [H, L]:
+    returns (out, lse)."""
+    return _forward_lse("h3attn_forward_lse", q, k, v, out, lse,
+                        1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale))
+
+
+def h3attn_forward_log2_lse(q, k, vt, out=None, lse=None):
+    """h3attn_forward_log2 that also returns each row's natural log-sum-exp, fp32 [H, L]:
+    returns (out, lse)."""
+    return _forward_lse("h3attn_forward_log2_lse", q, k, vt, out, lse, None)
 
 
 def h3attn_attention_backward(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, workspace=None,
@@ -294,10 +314,7 @@ def h3attn_attention_backward(q, k, v, out, dout, lse, dq=None, dk=None, dv=None
     return dq, dk, dv
 
 
-def h3attn_qk_prologue_backward(q, k, gamma_q, gamma_k, pos_thw, dq, dk, dgamma_q=None, dgamma_k=None,
-                                workspace=None):
-    """In place: dq, dk (gradients w.r.t. the prologue outputs) become the gradients w.r.t. the
-    raw q, k; returns (dgamma_q, dgamma_k), fp32 [128]."""
+def _prologue_backward(fn, q, k, gamma_q, gamma_k, pos_thw, dq, dk, dgamma_q, dgamma_k, workspace, q_scale):
     import torch
     L, H = _lh(q)
     dev = q.device
@@ -317,12 +334,31 @@ def h3attn_qk_prologue_backward(q, k, gamma_q, gamma_k, pos_thw, dq, dk, dgamma_
     if workspace.device != dev or workspace.numel() * workspace.element_size() < nbytes or not workspace.is_contiguous():
         raise ValueError(f"workspace must be a contiguous buffer of >= {nbytes} bytes on {dev}")
     with torch.cuda.device(dev):
-        st = lib.h3attn_qk_prologue_backward(q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(),
-                                             pos_thw.data_ptr(), dq.data_ptr(), dk.data_ptr(), dgamma_q.data_ptr(),
-                                             dgamma_k.data_ptr(), workspace.data_ptr(), L, H,
-                                             torch.cuda.current_stream(dev).cuda_stream)
-    _raise_on(lib, "h3attn_qk_prologue_backward", st)
+        args = (q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(), pos_thw.data_ptr(), dq.data_ptr(),
+                dk.data_ptr(), dgamma_q.data_ptr(), dgamma_k.data_ptr(), workspace.data_ptr(), L, H)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        if q_scale is None:
+            st = lib.h3attn_qk_prologue_backward(*args, stream)
+        else:
+            st = lib.h3attn_qk_prologue_backward_scaled(*args, float(q_scale), stream)
+    _raise_on(lib, fn, st)
     return dgamma_q, dgamma_k
+
+
+def h3attn_qk_prologue_backward(q, k, gamma_q, gamma_k, pos_thw, dq, dk, dgamma_q=None, dgamma_k=None,
+                                workspace=None):
+    """In place: dq, dk (gradients w.r.t. the prologue outputs) become the gradients w.r.t. the
+    raw q, k; returns (dgamma_q, dgamma_k), fp32 [128]."""
+    return _prologue_backward("h3attn_qk_prologue_backward", q, k, gamma_q, gamma_k, pos_thw, dq, dk, dgamma_q,
+                              dgamma_k, workspace, None)
+
+
+def h3attn_qk_prologue_backward_scaled(q, k, gamma_q, gamma_k, pos_thw, dq, dk, q_scale: float, dgamma_q=None,
+                                       dgamma_k=None, workspace=None):
+    """h3attn_qk_prologue_backward of h3attn_qk_prologue_scaled's prologue (dq: the gradient
+    w.r.t. Q's scaled output); returns (dgamma_q, dgamma_k)."""
+    return _prologue_backward("h3attn_qk_prologue_backward_scaled", q, k, gamma_q, gamma_k, pos_thw, dq, dk,
+                              dgamma_q, dgamma_k, workspace, q_scale)
 
 
 def abi_version() -> int:

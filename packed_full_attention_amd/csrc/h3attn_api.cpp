@@ -163,6 +163,12 @@ int h3attn_forward_lse(const void* q, const void* k, const void* v, void* out, f
   return forward(q, k, v, out, L, H, scale, false, stream, lse);
 }
 
+int h3attn_forward_log2_lse(const void* q, const void* k, const void* vt, void* out, float* lse, int64_t L,
+                            int32_t H, hipStream_t stream) {
+  if (!lse) return fail(H3A_EINVAL, "null pointer argument%s");
+  return forward(q, k, vt, out, L, H, 1.0f, true, stream, lse);
+}
+
 int64_t h3attn_rope_table_bytes(int64_t L, int32_t H) {
   uint64_t bytes = 0;
   if (check_shape(L, H, &bytes) != H3A_OK) return -1;
@@ -260,12 +266,14 @@ int64_t h3attn_qk_prologue_backward_workspace_bytes(int64_t L, int32_t H) {
   return h3attn::prologue_backward_workspace_bytes(L);
 }
 
-int h3attn_qk_prologue_backward(const void* q, const void* k, const float* gamma_q, const float* gamma_k,
-                                const int32_t* pos_thw, void* dq, void* dk, float* dgamma_q,
-                                float* dgamma_k, void* workspace, int64_t L, int32_t H,
-                                hipStream_t stream) {
+namespace {
+
+int prologue_backward(const void* q, const void* k, const float* gamma_q, const float* gamma_k,
+                      const int32_t* pos_thw, void* dq, void* dk, float* dgamma_q, float* dgamma_k, void* workspace,
+                      int64_t L, int32_t H, float q_scale, hipStream_t stream) {
   if (!q || !k || !gamma_q || !gamma_k || !pos_thw || !dq || !dk || !dgamma_q || !dgamma_k || !workspace)
     return fail(H3A_EINVAL, "null pointer argument%s");
+  if (!(isfinite(q_scale) && q_scale > 0.0f)) return fail(H3A_EINVAL, "q_scale must be finite and > 0%s");
   uint64_t bytes = 0;
   if (int s = check_shape(L, H, &bytes)) return s;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(dq, 16) || !aligned(dk, 16))
@@ -289,9 +297,27 @@ int h3attn_qk_prologue_backward(const void* q, const void* k, const float* gamma
   const hipError_t e = h3attn::launch_qk_prologue_backward(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), gamma_q, gamma_k, pos_thw,
       static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), dgamma_q, dgamma_k, static_cast<float*>(workspace), L,
-      H, stream);
+      H, q_scale, stream);
   if (e != hipSuccess) return fail(H3A_EHIP, "prologue backward launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+int h3attn_qk_prologue_backward(const void* q, const void* k, const float* gamma_q, const float* gamma_k,
+                                const int32_t* pos_thw, void* dq, void* dk, float* dgamma_q,
+                                float* dgamma_k, void* workspace, int64_t L, int32_t H,
+                                hipStream_t stream) {
+  return prologue_backward(q, k, gamma_q, gamma_k, pos_thw, dq, dk, dgamma_q, dgamma_k, workspace, L, H, 1.0f,
+                           stream);
+}
+
+int h3attn_qk_prologue_backward_scaled(const void* q, const void* k, const float* gamma_q, const float* gamma_k,
+                                       const int32_t* pos_thw, void* dq, void* dk, float* dgamma_q,
+                                       float* dgamma_k, void* workspace, int64_t L, int32_t H, float q_scale,
+                                       hipStream_t stream) {
+  return prologue_backward(q, k, gamma_q, gamma_k, pos_thw, dq, dk, dgamma_q, dgamma_k, workspace, L, H, q_scale,
+                           stream);
 }
 
 }  // extern "C"

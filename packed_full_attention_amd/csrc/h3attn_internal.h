@@ -49,11 +49,13 @@ int64_t backward_workspace_bytes(int64_t L, int32_t H);
 int backward_block_threads();
 
 // Backward of the prologue (in place on dq, dk) and the gamma gradients;
-// workspace of prologue_backward_workspace_bytes(L) bytes.
+// workspace of prologue_backward_workspace_bytes(L) bytes.  q_scale: the
+// factor launch_qk_prologue applied to Q's output (dq is the gradient with
+// respect to that scaled output).
 hipError_t launch_qk_prologue_backward(const uint16_t* q, const uint16_t* k, const float* gamma_q,
                                        const float* gamma_k, const int32_t* pos, uint16_t* dq, uint16_t* dk,
                                        float* dgamma_q, float* dgamma_k, float* workspace, int64_t L, int32_t H,
-                                       hipStream_t stream);
+                                       float q_scale, hipStream_t stream);
 int64_t prologue_backward_workspace_bytes(int64_t L);
 
 // V^T = [H][128][Lp] bf16, Lp = L rounded up to 64, zeros past L.

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
 __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_bwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ gamma_q,
     const float* __restrict__ gamma_k, const int32_t* __restrict__ pos, uint16_t* __restrict__ dq,
-    uint16_t* __restrict__ dk, float* __restrict__ partial, int64_t L, int32_t H) {
+    uint16_t* __restrict__ dk, float* __restrict__ partial, int64_t L, int32_t H, float q_scale) {
   __shared__ float wsum[kWavesPerBlock][2 * kHeadDim];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t token = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -181,8 +181,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_bwd_kernel(
   float gqa[4], gqb[4], gka[4], gkb[4];  // gammas at the lane's channels
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    gqa[e] = gamma_q[ch_a + e];
-    gqb[e] = gamma_q[ch_b + e];
+    gqa[e] = gamma_q[ch_a + e] * q_scale;  // Q's effective weights, as in the forward
+    gqb[e] = gamma_q[ch_b + e] * q_scale;
     gka[e] = gamma_k[ch_a + e];
     gkb[e] = gamma_k[ch_b + e];
   }
@@ -310,10 +310,11 @@ __global__ __launch_bounds__(2 * kHeadDim) void gamma_reduce_kernel(const float*
   out[(int64_t)blockIdx.x * 2 * kHeadDim + c] = acc;
 }
 
-// The last stage: the n group sums, in order -> dgamma_q (c < 128), dgamma_k;
-// 16 loads in flight ahead of the adds.
+// The last stage: the n group sums, in order -> dgamma_q (c < 128, times
+// q_scale: Q's output carried gamma_q * q_scale), dgamma_k; 16 loads in flight
+// ahead of the adds.
 __global__ __launch_bounds__(2 * kHeadDim) void gamma_final_kernel(const float* __restrict__ in, float* __restrict__ dgq,
-                                                                   float* __restrict__ dgk, int64_t n) {
+                                                                   float* __restrict__ dgk, int64_t n, float q_scale) {
   const int c = threadIdx.x;
   float acc = 0.f;
   for (int64_t r0 = 0; r0 < n; r0 += 16) {
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(2 * kHeadDim) void gamma_final_kernel(const float* 
     for (int i = 0; i < 16; ++i)
       if (r0 + i < n) acc += x[i];
   }
-  if (c < kHeadDim) dgq[c] = acc;
+  if (c < kHeadDim) dgq[c] = acc * q_scale;
   else dgk[c - kHeadDim] = acc;
 }
 
@@ -390,18 +391,19 @@ int64_t prologue_backward_workspace_bytes(int64_t L) {
 hipError_t launch_qk_prologue_backward(const uint16_t* q, const uint16_t* k, const float* gamma_q,
                                        const float* gamma_k, const int32_t* pos, uint16_t* dq, uint16_t* dk,
                                        float* dgamma_q, float* dgamma_k, float* workspace, int64_t L, int32_t H,
-                                       hipStream_t stream) {
+                                       float q_scale, hipStream_t stream) {
   const int64_t nb = bwd_blocks(L), ng = bwd_groups(L);
   float* partial = workspace;
   float* groups = workspace + nb * 2 * kHeadDim;
   hipLaunchKernelGGL(qk_prologue_bwd_kernel, dim3((unsigned)nb), dim3(kWavesPerBlock * 64), 0, stream, q, k,
-                     gamma_q, gamma_k, pos, dq, dk, partial, L, H);
+                     gamma_q, gamma_k, pos, dq, dk, partial, L, H, q_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gamma_reduce_kernel, dim3((unsigned)ng), dim3(2 * kHeadDim), 0, stream, partial, groups, nb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gamma_final_kernel, dim3(1), dim3(2 * kHeadDim), 0, stream, groups, dgamma_q, dgamma_k, ng);
+  hipLaunchKernelGGL(gamma_final_kernel, dim3(1), dim3(2 * kHeadDim), 0, stream, groups, dgamma_q, dgamma_k, ng,
+                     q_scale);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ def test_header_declares_the_expected_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.h3attn_abi_version() == 4
+    assert lib.h3attn_abi_version() == 5
 
 
 def test_strerror_strings(lib):
@@ -130,6 +130,23 @@ def test_fused_entry_points_reject(lib):
     for out in (A, B + 256, C + 1024, G - 256, P + 4096):
         assert fq(out=out) == 1 and "overlap" in lib.h3attn_last_error().decode()
     assert fq(L=1 << 31) == 2
+
+
+def test_training_entry_points_reject(lib):
+    fl = lambda **kw: lib.h3attn_forward_log2_lse(kw.get("q", A), B, kw.get("vt", C), kw.get("out", O),
+                                                  kw.get("lse", G), kw.get("L", 160), 4, None)
+    for kw in (dict(q=None), dict(vt=None), dict(out=None), dict(lse=None)):
+        assert fl(**kw) == 1 and "null" in lib.h3attn_last_error().decode()
+    assert fl(lse=G + 2) == 1 and "aligned" in lib.h3attn_last_error().decode()
+    assert fl(lse=A + 512) == 1 and "overlap" in lib.h3attn_last_error().decode()
+    assert fl(L=0) == 1
+    pb = lambda **kw: lib.h3attn_qk_prologue_backward_scaled(A, B, G, G + 512, P, C, O, G + 1024, G + 1536,
+                                                             kw.get("ws", G + 4096), kw.get("L", 160), 4,
+                                                             kw.get("s", 0.1275), None)
+    for s_ in (0.0, -2.0, float("nan"), float("inf")):
+        assert pb(s=s_) == 1 and "q_scale" in lib.h3attn_last_error().decode()
+    assert pb(ws=None) == 1 and pb(L=-3) == 1
+    assert pb(ws=C + 64) == 1 and "overlap" in lib.h3attn_last_error().decode()
 
 
 @pytest.mark.parametrize("L,H,want", [(160, 4, 160 * 384), (1, 56, 384), (16500, 56, 16500 * 384), (0, 4, -1),

@@ -16,6 +16,8 @@ import torch
 import oracle
 from gates import dgamma_ok, gradient_ok
 from gpu_util import dev_bf16, dev_inputs, host_bits, host_f64
+from packed_full_attention_amd import (h3attn_forward_log2, h3attn_forward_log2_lse, h3attn_qk_prologue_backward_scaled,
+                                       h3attn_qk_prologue_scaled, h3attn_v_transpose)
 from packed_full_attention_amd import (h3attn_attention_backward, h3attn_forward, h3attn_forward_lse,
                                        h3attn_qk_prologue, h3attn_qk_prologue_backward)
 from packed_full_attention_amd import workloads as wl
@@ -247,3 +249,69 @@ def test_whole_path_backward(inputs):
     # test_prologue_backward): they take the gradient gate.
     _check("whole path dgamma_q", gradient_ok(dgq.cpu().numpy(), rgq))
     _check("whole path dgamma_k", gradient_ok(dgk.cpu().numpy(), rgk))
+
+
+# ------------------------------------------------------------------ the scale-folded training step
+
+Q_SCALE = float(np.float32(SCALE * math.log2(math.e)))
+LN2 = math.log(2.0)
+
+
+@pytest.mark.parametrize("idx", (0, 1, 2))
+def test_forward_log2_lse(inputs, idx):
+    """The log2 kernel's log-sum-exp: ln sum_j 2^<q', k_j> = ln sum_j exp(ln 2 <q', k_j>); out
+    is the plain log2 forward's, bit for bit."""
+    inp = inputs(idx)
+    q, k, v, gq, gk, pos = dev_inputs(inp)
+    h3attn_qk_prologue_scaled(q, k, gq, gk, pos, Q_SCALE)
+    vt = h3attn_v_transpose(v)
+    out, lse = h3attn_forward_log2_lse(q, k, vt)
+    plain = h3attn_forward_log2(q, k, vt)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
+    ref = oracle.log_sum_exp_rows(host_f64(q), host_f64(k), LN2)
+    err = float(np.abs(lse.cpu().numpy().astype(np.float64) - ref).max())
+    print(f"log2 lse workload {idx}: max-abs {err:.3e}")
+    assert err <= LSE_TOL
+
+
+def test_prologue_backward_scale_one_is_plain(inputs):
+    inp = inputs(1)
+    L, H = inp.workload.seq_len, inp.workload.heads
+    q, k, _, gq, gk, pos = dev_inputs(inp)
+    res = []
+    for scaled in (False, True):
+        dq, dk = dev_bf16(_bf16_normal((L, H, 128), 60)), dev_bf16(_bf16_normal((L, H, 128), 61))
+        if scaled:
+            g = h3attn_qk_prologue_backward_scaled(q, k, gq, gk, pos, dq, dk, 1.0)
+        else:
+            g = h3attn_qk_prologue_backward(q, k, gq, gk, pos, dq, dk)
+        torch.cuda.synchronize()
+        res.append([host_bits(dq), host_bits(dk), g[0].cpu().numpy(), g[1].cpu().numpy()])
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("idx", (1, 2))
+def test_whole_path_backward_scale_folded(inputs, idx):
+    """Raw inputs -> scaled prologue (q' = c q) -> log2 forward with lse -> attention
+    backward on q' at scale ln 2 -> scaled prologue backward, against the oracle's
+    gradients of the plain path at scale 1/sqrt(128)."""
+    inp = inputs(idx)
+    q, k, v, gq, gk, pos = dev_inputs(inp)
+    q_raw, k_raw = q.clone(), k.clone()
+    h3attn_qk_prologue_scaled(q, k, gq, gk, pos, Q_SCALE)
+    L, H = inp.workload.seq_len, inp.workload.heads
+    do_bits = _bf16_normal((L, H, 128), 4343 + idx)
+    out, lse = h3attn_forward_log2_lse(q, k, h3attn_v_transpose(v))
+    dq, dk, dv = h3attn_attention_backward(q, k, v, out, dev_bf16(do_bits), lse, scale=LN2)
+    dgq, dgk = h3attn_qk_prologue_backward_scaled(q_raw, k_raw, gq, gk, pos, dq, dk, Q_SCALE)
+    torch.cuda.synchronize()
+    rq, rk, rv, rgq, rgk = oracle.packed_attention_backward(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"),
+                                                            inp.gamma_q, inp.gamma_k, inp.pos, _as_f64(do_bits),
+                                                            SCALE)
+    _check(f"scale-folded path {idx} dq", gradient_ok(host_f64(dq), rq))
+    _check(f"scale-folded path {idx} dk", gradient_ok(host_f64(dk), rk))
+    _check(f"scale-folded path {idx} dv", gradient_ok(host_f64(dv), rv))
+    _check(f"scale-folded path {idx} dgamma_q", gradient_ok(dgq.cpu().numpy(), rgq))
+    _check(f"scale-folded path {idx} dgamma_k", gradient_ok(dgk.cpu().numpy(), rgk))
