@@ -20,11 +20,12 @@
 //
 // Two kernels; each wave owns 32 rows of one head and the workgroup streams
 // the other side through LDS in 64-row tiles:
-//   dq (8 waves, 256 queries): streams K and V.  Per tile S^T = K Q^T and
-//        dP^T = V dO^T (K, V row operands from LDS; Q^T, dO^T held in
+//   dq (8 waves, 256 queries): streams K and V.  Per 32-key block S^T = K Q^T
+//        and dP^T = V dO^T (K, V row operands from LDS; Q^T, dO^T held in
 //        registers), dS^T from them, dQ^T += K^T dS^T (K^T gathered by
-//        transposing LDS reads).  It also computes delta for its rows and
-//        leaves -lse log2(e) and -delta per row for the second kernel.
+//        transposing LDS reads), software-pipelined over the blocks.  It
+//        also computes delta for its rows and leaves -lse log2(e) and -delta
+//        per row for the second kernel.
 //   dkdv (4 waves, 128 keys): streams Q, dO and those two statistics.  Per
 //        32-query block S = Q K^T and dP - delta = dO V^T - delta (Q, dO from
 //        LDS; K^T, V^T in registers), P and dS, dV^T += dO^T P and
@@ -38,8 +39,8 @@
 // registers (at two waves per SIMD the fused kernel spills; split into a dK
 // and a dV kernel it recomputes S once more and takes 11% longer).
 //
-// Tiles arrive by buffer_load_dwordx4 ... lds into a ring of three slots
-// (no VGPR staging), one barrier per tile; tiles are row-major with chunk c of
+// Tiles arrive by buffer_load_dwordx4 ... lds into a ring of four slots (no
+// VGPR staging), one barrier per tile; tiles are row-major with chunk c of
 // row r at c ^ swz(r) (conflict-free row and transposing reads).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
