@@ -137,7 +137,7 @@ def main() -> int:
                     help="run one elementwise copy of a known size first (for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by heads with no exchange, so run one process per GPU on its head share.",
               file=sys.stderr)
         return 2
