@@ -274,3 +274,33 @@ def test_scaled_path_no_writes_outside_buffers():
         h = host_bits(t)
         assert np.all(h[:guard] == sentinel) and np.all(h[-guard:] == sentinel)
     assert not np.any(host_bits(out_full)[guard:guard + n] == sentinel)
+
+
+# ------------------------------------------------------------------ one long head
+
+def test_long_single_head_scaled_and_fused_paths():
+    """L = 70001 tokens of one head (1094 key tiles, L mod 256 = 113, L mod 64 = 49,
+    positions up to 5000): sampled rows of the scale-folded path against the
+    oracle, and the fused path bit-identical to it."""
+    from packed_full_attention_amd import h3attn_forward_log2_qprologue, h3attn_k_prologue_table
+    L, H = 70001, 1
+    inp = wl.random_document(L, H, seed=7001, pos_max=5000)
+    print(f"long single head: L={L} H={H}", flush=True)
+    q, k, v = run_prologue(inp)
+    vt = h3attn_v_transpose(v)
+    out = h3attn_forward_log2(q, k, vt)
+    q2, k2, _, gq, gk, pos = dev_inputs(inp)
+    cs = h3attn_k_prologue_table(k2, gk, pos)
+    out2 = h3attn_forward_log2_qprologue(q2, k2, vt, gq, cs, Q_SCALE)
+    torch.cuda.synchronize()
+    got_all = host_bits(out)
+    assert np.array_equal(host_bits(out2), got_all)
+    rng = np.random.default_rng(7002)
+    rows = np.unique(np.concatenate([[0, 1, L - 50, L - 49, L - 2, L - 1], rng.choice(L, 40, replace=False)]))
+    heads = np.zeros_like(rows)
+    ref = oracle.packed_attention_sampled(head_f64(inp.q), head_f64(inp.k), head_f64(inp.v), inp.gamma_q,
+                                          inp.gamma_k, inp.pos, SCALE, rows, heads)
+    got = wl.bf16_bits_to_f32(got_all[rows, 0]).astype(np.float64)
+    ok, e = attention_ok(got, ref)
+    print(f"long single head ({len(rows)} rows): {e}")
+    assert ok, e
