@@ -25,7 +25,9 @@
 // walks through in chunks of kPasses 4-row passes whose loads are all in flight
 // together; kPasses is chosen per H so the chunks waste the fewest row slots
 // (14 passes = 56 rows for H = 56: each chunk is exactly one tensor's rows of
-// the token).
+// the token).  A K-only form walks K's H rows alone and also stores each
+// token's 48 cosines and sines, which the attention kernel's fused Q prologue
+// reads instead of evaluating them again.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
