@@ -358,6 +358,24 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
   dma_wait();
   __syncthreads();
 
+  // A wave none of whose rows exists (only in a head's last, partial query
+  // tile) carries its share of the ring DMA and takes part in every barrier,
+  // computing nothing: its SIMD's matrix core is left to the other wave.
+  if (qtile * kRows + wave * 32 >= L) {
+#pragma unroll
+    for (int j = 0; j < kDqPieces; ++j) piece(2, j);
+    dma_wait_all_but<kDqPieces>();
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+#pragma unroll
+      for (int j = 0; j < kDqPieces; ++j) piece(t + 3, j);
+      dma_wait_all_but<kDqPieces>();
+      __syncthreads();
+    }
+    dma_wait();
+    return;
+  }
+
   // Block (0, 0)'s scores.
   f32x16_t sa = f32x16_t{}, da = f32x16_t{};
 #pragma unroll
