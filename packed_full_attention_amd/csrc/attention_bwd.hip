@@ -104,13 +104,6 @@ __device__ __forceinline__ void dma_row_piece(const uint16_t* base, int64_t tok_
   lds_dma_dwordx4(rsrc, d.off[it], __builtin_amdgcn_readfirstlane(lds_tile + (it * W + wave) * 1024));
 }
 
-template <int W>
-__device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t tok_stride, int t, int L,
-                                         const DmaOffsets<W>& d, uint32_t lds_tile, int wave) {
-#pragma unroll
-  for (int it = 0; it < dma_per_wave<W>(); ++it) dma_row_piece<W>(base, tok_stride, t, L, d, lds_tile, wave, it);
-}
-
 // The 64 fp32 values v[t*64 .. t*64+63] of an n-value vector (zeros past n)
 // into LDS at lds: one 1 KiB piece, whose first 256 bytes are those values.
 __device__ __forceinline__ void dma_vec(const float* v, int t, int n, uint32_t lds, int lane) {
@@ -148,17 +141,6 @@ __device__ __forceinline__ bf16x8_t tr_operand(const lds_char* tile, int dblk, i
   const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + 4096 * j + (a.tr0 ^ (64u * dblk))));
   const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + 4096 * j + (a.tr1 ^ (64u * dblk))));
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// The 16 slots of an accumulator, rounded to bf16, as two B operands: slots
-// 0..7 (rows 4g.., 8+4g..) and 8..15 (rows 16+4g.., 24+4g..).
-__device__ __forceinline__ void pack_operands(const float (&x)[16], bf16x8_t (&p)[2]) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-    p[h] = __builtin_bit_cast(bf16x8_t, u32x4_t{pack_bf16x2(x[8 * h], x[8 * h + 1]),
-                                                pack_bf16x2(x[8 * h + 2], x[8 * h + 3]),
-                                                pack_bf16x2(x[8 * h + 4], x[8 * h + 5]),
-                                                pack_bf16x2(x[8 * h + 6], x[8 * h + 7])});
 }
 
 // One 32-row block of a [L][H][128] tensor as the B operand of a 32x32x16
