@@ -70,7 +70,8 @@ extern "C" {
  * the end; accurate fp32 sine and cosine.
  *
  *   q, k     bf16 [L][H][128], read and rewritten in place; 16-byte aligned;
- *            the two ranges must not overlap.
+ *            the two ranges must not overlap each other or gamma_q, gamma_k,
+ *            pos_thw.
  *   gamma_q, gamma_k  fp32 [128] RMSNorm weights, shared by all heads;
  *            4-byte aligned.
  *   pos_thw  int32 [L][3] per-token (t, h, w) positions; 4-byte aligned.
@@ -157,7 +158,8 @@ int h3attn_forward_log2(const void* q, const void* k, const void* vt, void* out,
  *   bits), and rope_cs[l][a] = cos(phi_a), rope_cs[l][48 + a] = sin(phi_a)
  *   for the 48 angles phi_a of token l (fp32 [L][96], as the prologue
  *   evaluates them).  rope_cs: caller-owned device memory of
- *   h3attn_rope_table_bytes(L, H) bytes, 16-byte aligned, not overlapping k.
+ *   h3attn_rope_table_bytes(L, H) bytes, 16-byte aligned; k, rope_cs, gamma_k
+ *   and pos_thw must not overlap.
  *
  * h3attn_forward_log2_qprologue: h3attn_forward_log2 of q' = the scaled
  *   prologue of the raw q (as h3attn_qk_prologue_scaled computes it with

@@ -78,6 +78,11 @@ int prologue(void* q, void* k, const float* gamma_q, const float* gamma_k, const
     return fail(H3A_EINVAL, "gamma_q, gamma_k and pos_thw must be 4-byte aligned%s");
   if (!(isfinite(q_scale) && q_scale > 0.0f)) return fail(H3A_EINVAL, "q_scale must be finite and > 0%s");
   if (overlap(q, bytes, k, bytes)) return fail(H3A_EINVAL, "q and k overlap%s");
+  // q and k are rewritten while the weights and positions are read.
+  const uint64_t pbytes = (uint64_t)L * 12;
+  for (const void* w : {q, k})
+    if (overlap(w, bytes, gamma_q, 512) || overlap(w, bytes, gamma_k, 512) || overlap(w, bytes, pos_thw, pbytes))
+      return fail(H3A_EINVAL, "q or k overlaps gamma_q, gamma_k or pos_thw%s");
   if (h3attn::prologue_grid_blocks(L) * 256 >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "prologue grid too large for L%s");
   const hipError_t e = h3attn::launch_qk_prologue(static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
@@ -188,6 +193,8 @@ int h3attn_k_prologue_table(void* k, const float* gamma_k, const int32_t* pos_th
   if (overlap(rope_cs, tbytes, k, bytes) || overlap(rope_cs, tbytes, gamma_k, 512) ||
       overlap(rope_cs, tbytes, pos_thw, (uint64_t)L * 12))
     return fail(H3A_EINVAL, "rope_cs overlaps k, gamma_k or pos_thw%s");
+  if (overlap(k, bytes, gamma_k, 512) || overlap(k, bytes, pos_thw, (uint64_t)L * 12))
+    return fail(H3A_EINVAL, "k overlaps gamma_k or pos_thw%s");
   if (h3attn::prologue_grid_blocks(L) * 256 >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "prologue grid too large for L%s");
   const hipError_t e =

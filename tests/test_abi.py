@@ -91,6 +91,15 @@ def test_forward_rejects(lib, kw, code, msg):
     assert msg in lib.h3attn_last_error().decode()
 
 
+def test_prologue_rejects_weights_or_positions_inside_q_or_k(lib):
+    # q = A, k = B, each 160 * 4 * 128 * 2 bytes: gammas or positions inside either are rejected.
+    for kw in (dict(gq=A + 1024), dict(gk=B + 4096), dict(pos=A + 256), dict(pos=B)):
+        assert prologue(lib, **kw) == 1 and "overlaps" in lib.h3attn_last_error().decode()
+    assert lib.h3attn_k_prologue_table(B, B + 512, P, C, 160, 4, None) == 1
+    assert "k overlaps" in lib.h3attn_last_error().decode()
+    assert lib.h3attn_k_prologue_table(B, G, B + 2048, C, 160, 4, None) == 1
+
+
 def test_scaled_entry_points_reject(lib):
     f = lambda **kw: lib.h3attn_qk_prologue_scaled(kw.get("q", A), B, G, G + 512, P, kw.get("L", 160), 4,
                                                      kw.get("s", 0.1275), None)
