@@ -304,3 +304,33 @@ def test_long_single_head_scaled_and_fused_paths():
     ok, e = attention_ok(got, ref)
     print(f"long single head ({len(rows)} rows): {e}")
     assert ok, e
+
+
+# ------------------------------------------------------------------ extreme score ranges
+
+@pytest.mark.parametrize("alpha", [3.0, 8.0])
+def test_dominant_keys_and_overflowing_weights(alpha):
+    """Query i = alpha * k[j(i)] for a random key j(i): that key's score exceeds the
+    others by about 30 (alpha 3) or 80 (alpha 8) in natural units, so the output is
+    nearly v[j(i)].  The dominant key usually sits in a later tile than the first,
+    so the exponent offset must move mid-row; at alpha 8 a tile's base-2 weights
+    reach 2^130 and overflow fp32, which must also lead to a rebase, not to inf or
+    NaN.  Plain and scale-folded kernels against the oracle."""
+    from packed_full_attention_amd import h3attn_forward
+    L, H = 700, 2
+    rng = np.random.default_rng(int(alpha * 10))
+    k = rng.standard_normal((L, H, 128)).astype(np.float32)
+    v = rng.standard_normal((L, H, 128)).astype(np.float32)
+    j = rng.integers(0, L, size=(L, H))
+    q = alpha * k[j, np.arange(H)[None, :], :]
+    qb, kb, vb = bf16_of(q), bf16_of(k), bf16_of(v)
+    f = lambda b: wl.bf16_bits_to_f32(b).astype(np.float64)
+    out_plain = h3attn_forward(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), scale=SCALE)
+    q2 = bf16_of(f(qb) * Q_SCALE)
+    out_log2 = h3attn_forward_log2(dev_bf16(q2), dev_bf16(kb), h3attn_v_transpose(dev_bf16(vb)))
+    torch.cuda.synchronize()
+    for name, got, ref in (("plain", host_f64(out_plain), oracle.attention(f(qb), f(kb), f(vb), SCALE)),
+                           ("log2", host_f64(out_log2), oracle.attention(f(q2), f(kb), f(vb), LN2))):
+        ok, e = attention_ok(got, ref)
+        print(f"alpha {alpha} {name}: {e}")
+        assert ok, (name, e)
