@@ -153,7 +153,8 @@ def test_path_parity_sampled_long(inputs, idx):
 # ------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("L,H", [(1, 1), (2, 3), (3, 1), (31, 2), (32, 1), (33, 1), (63, 1), (64, 2),
-                                 (65, 1), (127, 1), (128, 2), (129, 1), (200, 3), (1000, 2)])
+                                 (65, 1), (127, 1), (128, 2), (129, 1), (200, 3), (1000, 2),
+                                 (300, 128), (513, 97)])
 def test_path_edge_lengths(L, H):
     inp = wl.random_document(L, H, seed=100 + L + H, pos_max=2000)
     q, k, v, gq, gk, pos = dev_inputs(inp)
