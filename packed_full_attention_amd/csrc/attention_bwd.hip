@@ -196,10 +196,12 @@ __device__ __forceinline__ void block_tile(int b, int H, int n_full, int& head, 
 // Slot k with k % 3 == 2 holds dQ MFMA k / 3 (= 4 jj + dblk); every other
 // slot holds MFMA n = 2 (k / 3) + k % 3 of the next block, S for even n and dP
 // for odd n, k-step n / 2.  Element e of this block's weights starts at slot
-// 3e / 2 (exponent), then its exponential, then dS, and each bf16 pair is
-// packed the slot after its second dS.  K and V come through rings of four
-// 64-key tiles (128 KiB); the step of (t, 0) starts the DMA of tile t + 2 into
-// the slot of tile t - 2 and ends with the tile's one barrier.
+// e (exponent), then its exponential, then dS, and each bf16 pair is packed
+// the slot after its second dS; the last slots hold matrix work only (this
+// front-loaded order measured 1% faster than one spread over all 24 slots).
+// K and V come through rings of four 64-key tiles (128 KiB); the step of
+// (t, 0) starts the DMA of tile t + 2 into the slot of tile t - 2 and ends
+// with the tile's one barrier.
 //
 // The weights are computed halved, P/2 = exp2(c S - lse log2 e - 1) with the
 // exponential's output clamped to [0, 1] (a free instruction modifier), and dQ
@@ -221,7 +223,9 @@ __device__ __forceinline__ bf16x8_t dq_operand(int k, const lds_char* nk, const 
   return row_operand((n & 1) ? nv : nk, kbn, n >> 1, a);
 }
 
-constexpr int dq_slot(int e) { return (3 * e) / 2; }
+constexpr int dq_slot(int e) { return e; }
+// Slots a step runs: the 24 matrix slots, and after them any the last pair's pack needs.
+constexpr int kDqSteps = dq_slot(15) + 4 > 24 ? dq_slot(15) + 4 : 24;
 
 // One step: next block in K/V slots nk, nv (half kbn), previous block in K
 // slot pk (half kbp; kPrev: there is one).  s_c, dp_c: this block's S^T and
@@ -245,7 +249,7 @@ __device__ __forceinline__ void dq_step(const lds_char* nk, const lds_char* nv, 
   float xa[16], p[16], x[16];
   uint32_t pair[8];
 #pragma unroll
-  for (int k = 0; k < dq_slot(15) + 4; ++k) {
+  for (int k = 0; k < kDqSteps; ++k) {
     dma(k);
     if (k < 24) {
       const int kk = k + kAheadDq;
