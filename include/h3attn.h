@@ -23,9 +23,10 @@
  *     Batch is not an argument: a batch is a replication axis, so callers
  *     issue one call per document.
  *   - All pointers are device memory owned by the caller.  The library
- *     allocates nothing, keeps no state between calls, and only enqueues work
- *     on `stream` (0 = the null stream): the calls return before the GPU
- *     finishes, and the caller synchronises.
+ *     allocates nothing and only enqueues work on `stream` (0 = the null
+ *     stream): the calls return before the GPU finishes, and the caller
+ *     synchronises.  Between calls it keeps only the text of the calling
+ *     thread's last error (h3attn_last_error, thread-local).
  *   - Arguments are validated on the host before any launch; a rejected call
  *     launches nothing and leaves every buffer untouched.  There is no
  *     fallback path.  Device data is not inspected: non-finite inputs
@@ -51,8 +52,11 @@ extern "C" {
 #define H3A_OK 0            /* success (work enqueued)                               */
 #define H3A_EINVAL 1        /* null pointer, L <= 0, H <= 0, misalignment, overlap,   */
                             /* or a non-finite / non-positive scale or q_scale        */
-#define H3A_EUNSUPPORTED 2  /* geometry outside the supported range (L >= 2^31,       */
-                            /* grid or size overflow)                                 */
+#define H3A_EUNSUPPORTED 2  /* geometry outside the supported range: L >= 2^31, a    */
+                            /* grid or size overflow, or a tile whose bytes span more */
+                            /* than 2^32 (the attention calls need 63*H*256 + 256 <=  */
+                            /* 2^32 - 1; the vt calls 254*Lp + 128 <= 2^32 - 1; the   */
+                            /* prologue calls 2H + 64 < 2^31)                         */
 #define H3A_EHIP 3          /* the HIP launch reported an error                       */
 
 /*

@@ -622,6 +622,9 @@ __global__ __launch_bounds__(64 * kFusedWaves, 1) void attention_bwd_dkdv_kernel
 int64_t backward_grid_blocks(int64_t L, int32_t H) { return ((L + kRows - 1) / kRows) * (int64_t)H; }
 int64_t backward_workspace_bytes(int64_t L, int32_t H) { return 2 * (int64_t)H * ((L + kTile - 1) / kTile * kTile) * 4; }
 int backward_block_threads() { return kThreads; }
+// One past the last byte a row-tile DMA reads, from the tile's first byte (row
+// kTile - 1, chunk 15); the offsets are 32-bit (see dma_offsets).
+int64_t backward_tile_dma_end(int32_t H) { return (int64_t)(kTile - 1) * H * kD * 2 + kD * 2; }
 
 hipError_t launch_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* out, const uint16_t* dout, const float* lse,

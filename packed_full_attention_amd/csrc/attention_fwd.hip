@@ -795,6 +795,13 @@ __global__ __launch_bounds__(kVtThreads) void v_transpose_kernel(const uint16_t*
 int64_t attention_grid_blocks(int64_t L, int32_t H) { return ((L + kBM - 1) / kBM) * (int64_t)H; }
 int attention_block_threads() { return kThreads; }
 
+// One past the last byte, counted from the tile's first byte, that a tile DMA
+// reads (dma_offsets: row kBN - 1, chunk 15; vt_dma_offsets: channel row
+// kD - 1, chunk 7).  The per-lane offsets are 32-bit and the buffer size is
+// clamped to 2^32 - 1, so a geometry whose end exceeds that would wrap.
+int64_t row_tile_dma_end(int32_t H) { return (int64_t)(kBN - 1) * H * kD * 2 + kD * 2; }
+int64_t vt_tile_dma_end(int64_t L) { return (int64_t)(kD - 1) * vt_padded_length(L) * 2 + kBN * 2; }
+
 int64_t vt_padded_length(int64_t L) { return (L + kBN - 1) / kBN * kBN; }
 int64_t vt_bytes(int64_t L, int32_t H) { return (int64_t)H * kD * vt_padded_length(L) * 2; }
 int64_t transpose_grid_blocks(int64_t L, int32_t H) { return vt_padded_length(L) / kBN * (int64_t)H; }

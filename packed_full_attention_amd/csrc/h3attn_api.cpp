@@ -7,6 +7,7 @@
 #include "h3attn.h"
 
 #include <math.h>
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -44,6 +45,31 @@ int check_shape(int64_t L, int32_t H, uint64_t* bytes) {
   const __int128 elems = (__int128)L * H * H3ATTN_HEAD_DIM;
   if (elems * 2 > ((__int128)1 << 62)) return fail(H3A_EUNSUPPORTED, "L*H*128 too large%s");
   *bytes = (uint64_t)(elems * 2);
+  return H3A_OK;
+}
+
+// The attention kernels address a tile through a buffer resource with 32-bit
+// per-lane byte offsets (and a 32-bit size), so every byte a tile DMA reads must
+// lie within 2^32 - 1 bytes of the tile's first byte; past that the offsets
+// would wrap and read other rows.  Such geometries are rejected.
+constexpr int64_t kMaxTileSpan = 0xffffffffLL;
+
+int check_row_tiles(int32_t H) {
+  if (h3attn::row_tile_dma_end(H) > kMaxTileSpan || h3attn::backward_tile_dma_end(H) > kMaxTileSpan)
+    return fail(H3A_EUNSUPPORTED, "H too large: a 64-token tile of [L][H][128] spans more than 2^32 bytes%s");
+  return H3A_OK;
+}
+
+int check_vt_tiles(int64_t L) {
+  if (h3attn::vt_tile_dma_end(L) > kMaxTileSpan)
+    return fail(H3A_EUNSUPPORTED, "L too large for vt: a 64-key tile of [H][128][Lp] spans more than 2^32 bytes%s");
+  return H3A_OK;
+}
+
+// The prologue kernels count a token's 2H head rows (Q's, then K's) in 32-bit
+// integers, in steps of up to 64 rows.
+int check_prologue_rows(int32_t H) {
+  if (2 * (int64_t)H + 64 > INT32_MAX) return fail(H3A_EUNSUPPORTED, "H too large for the prologue (2H + 64 >= 2^31)%s");
   return H3A_OK;
 }
 
@@ -85,6 +111,7 @@ int prologue(void* q, void* k, const float* gamma_q, const float* gamma_k, const
       return fail(H3A_EINVAL, "q or k overlaps gamma_q, gamma_k or pos_thw%s");
   if (h3attn::prologue_grid_blocks(L) * 256 >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "prologue grid too large for L%s");
+  if (int s = check_prologue_rows(H)) return s;
   const hipError_t e = h3attn::launch_qk_prologue(static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
                                                   gamma_q, gamma_k, pos_thw, L, H, q_scale, stream);
   if (e != hipSuccess) return fail(H3A_EHIP, "prologue launch failed: %s", hipGetErrorString(e));
@@ -112,6 +139,9 @@ int forward(const void* q, const void* k, const void* v, void* out, int64_t L, i
   }
   if (h3attn::attention_grid_blocks(L, H) * h3attn::attention_block_threads() >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "attention grid too large for (L, H)%s");
+  if (int s = check_row_tiles(H)) return s;
+  if (log2)
+    if (int s = check_vt_tiles(L)) return s;
   const hipError_t e = h3attn::launch_attention_forward(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       static_cast<uint16_t*>(out), lse, L, H, scale, log2, stream);
@@ -197,6 +227,7 @@ int h3attn_k_prologue_table(void* k, const float* gamma_k, const int32_t* pos_th
     return fail(H3A_EINVAL, "k overlaps gamma_k or pos_thw%s");
   if (h3attn::prologue_grid_blocks(L) * 256 >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "prologue grid too large for L%s");
+  if (int s = check_prologue_rows(H)) return s;
   const hipError_t e =
       h3attn::launch_k_prologue(static_cast<uint16_t*>(k), gamma_k, pos_thw, rope_cs, L, H, stream);
   if (e != hipSuccess) return fail(H3A_EHIP, "prologue launch failed: %s", hipGetErrorString(e));
@@ -218,6 +249,8 @@ int h3attn_forward_log2_qprologue(const void* q, const void* k, const void* vt, 
     return fail(H3A_EINVAL, "out overlaps q, k, vt, gamma_q or rope_cs%s");
   if (h3attn::attention_grid_blocks(L, H) * h3attn::attention_block_threads() >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "attention grid too large for (L, H)%s");
+  if (int s = check_row_tiles(H)) return s;
+  if (int s = check_vt_tiles(L)) return s;
   const hipError_t e = h3attn::launch_attention_forward_qprologue(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(vt),
       static_cast<uint16_t*>(out), gamma_q, rope_cs, L, H, q_scale, stream);
@@ -258,6 +291,7 @@ int h3attn_attention_backward(const void* q, const void* k, const void* v, const
   }
   if (h3attn::backward_grid_blocks(L, H) * h3attn::backward_block_threads() >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "backward grid too large for (L, H)%s");
+  if (int s = check_row_tiles(H)) return s;
   const hipError_t e = h3attn::launch_attention_backward(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, static_cast<uint16_t*>(dq),
@@ -301,6 +335,7 @@ int prologue_backward(const void* q, const void* k, const float* gamma_q, const 
   }
   if (h3attn::prologue_grid_blocks(L) * 256 >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "prologue grid too large for L%s");
+  if (int s = check_prologue_rows(H)) return s;
   const hipError_t e = h3attn::launch_qk_prologue_backward(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), gamma_q, gamma_k, pos_thw,
       static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), dgamma_q, dgamma_k, static_cast<float*>(workspace), L,

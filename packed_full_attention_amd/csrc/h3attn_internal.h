@@ -47,6 +47,7 @@ hipError_t launch_attention_backward(const uint16_t* q, const uint16_t* k, const
 int64_t backward_grid_blocks(int64_t L, int32_t H);
 int64_t backward_workspace_bytes(int64_t L, int32_t H);
 int backward_block_threads();
+int64_t backward_tile_dma_end(int32_t H);
 
 // Backward of the prologue (in place on dq, dk) and the gamma gradients;
 // workspace of prologue_backward_workspace_bytes(L) bytes.  q_scale: the
@@ -70,5 +71,13 @@ int transpose_block_threads();
 int64_t attention_grid_blocks(int64_t L, int32_t H);
 int attention_block_threads();
 int64_t prologue_grid_blocks(int64_t L);
+
+// The tile DMA of the attention kernels addresses a tile through a buffer
+// resource with 32-bit per-lane offsets: these give one past the last byte a
+// row-major tile ([L][H][128], 64 rows) or a V^T tile (128 channel rows of 64
+// keys) reads, counted from the tile's first byte.  Validation rejects any
+// geometry where that end exceeds 2^32 - 1.
+int64_t row_tile_dma_end(int32_t H);
+int64_t vt_tile_dma_end(int64_t L);
 
 }  // namespace h3attn

@@ -189,3 +189,60 @@ def test_binding_rejects_bad_tensors_on_cpu():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="no fallback"):
         b.load_library(str(tmp_path / "libh3attn.so"))
+
+
+# Geometries whose tile DMA offsets would pass 2^32 bytes (the kernels address a
+# tile through a buffer resource with 32-bit offsets): rejected, never launched.
+# Fake addresses 2^44 apart, so no size overlaps another range.
+FAR = [(i + 1) << 44 for i in range(12)]
+H_WRAP = 266305        # 63 * H * 256 + 256 > 2^32 - 1 (H = 266304 still fits)
+L_VT_WRAP = 16909313   # Lp = 16909376: 127 * 2 * Lp + 128 > 2^32 - 1
+
+
+def test_row_tile_span_rejected_on_every_attention_entry_point(lib):
+    L, H = 64, H_WRAP
+    q, k, v, out, lse, vt, gq, cs, dout, dq, dk, dv = FAR
+    ws = FAR[11] + (1 << 43)
+    calls = {
+        "forward": lambda: lib.h3attn_forward(q, k, v, out, L, H, 0.088, None),
+        "forward_lse": lambda: lib.h3attn_forward_lse(q, k, v, out, lse, L, H, 0.088, None),
+        "forward_log2": lambda: lib.h3attn_forward_log2(q, k, vt, out, L, H, None),
+        "forward_log2_lse": lambda: lib.h3attn_forward_log2_lse(q, k, vt, out, lse, L, H, None),
+        "forward_log2_qprologue": lambda: lib.h3attn_forward_log2_qprologue(q, k, vt, out, gq, cs, L, H, 0.1275,
+                                                                            None),
+        "attention_backward": lambda: lib.h3attn_attention_backward(q, k, v, out, dout, lse, dq, dk, dv, ws, L, H,
+                                                                    0.088, None),
+    }
+    for name, call in calls.items():
+        assert call() == 2, name
+        assert "2^32" in lib.h3attn_last_error().decode(), name
+
+
+def test_vt_tile_span_rejected_on_the_vt_entry_points(lib):
+    L, H = L_VT_WRAP, 1
+    q, k, out, lse, vt, gq, cs = FAR[:7]
+    for name, call in {
+        "forward_log2": lambda: lib.h3attn_forward_log2(q, k, vt, out, L, H, None),
+        "forward_log2_lse": lambda: lib.h3attn_forward_log2_lse(q, k, vt, out, lse, L, H, None),
+        "forward_log2_qprologue": lambda: lib.h3attn_forward_log2_qprologue(q, k, vt, out, gq, cs, L, H, 0.1275,
+                                                                            None),
+    }.items():
+        assert call() == 2, name
+        msg = lib.h3attn_last_error().decode()
+        assert "vt" in msg and "2^32" in msg, (name, msg)
+
+
+def test_prologue_row_count_overflow_rejected(lib):
+    L, H = 1, (1 << 30) - 31  # 2H + 64 > 2^31 - 1
+    q, k, gq, gk, pos, cs, dq, dk, dgq, dgk, ws = FAR[:11]
+    for name, call in {
+        "qk_prologue": lambda: lib.h3attn_qk_prologue(q, k, gq, gk, pos, L, H, None),
+        "qk_prologue_scaled": lambda: lib.h3attn_qk_prologue_scaled(q, k, gq, gk, pos, L, H, 0.5, None),
+        "k_prologue_table": lambda: lib.h3attn_k_prologue_table(k, gk, pos, cs, L, H, None),
+        "qk_prologue_backward": lambda: lib.h3attn_qk_prologue_backward(q, k, gq, gk, pos, dq, dk, dgq, dgk, ws, L,
+                                                                        H, None),
+        "qk_prologue_backward_scaled": lambda: lib.h3attn_qk_prologue_backward_scaled(
+            q, k, gq, gk, pos, dq, dk, dgq, dgk, ws, L, H, 0.5, None),
+    }.items():
+        assert call() == 2, name
+        assert "prologue" in lib.h3attn_last_error().decode(), name
