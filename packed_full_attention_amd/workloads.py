@@ -197,3 +197,17 @@ def scale_rows_bf16(bits: np.ndarray, rows: np.ndarray, factor_log2: int) -> np.
         f = bf16_bits_to_f32(out[rows]) * np.float32(2.0 ** factor_log2)
         out[rows] = bf16_bits(f)
     return out
+
+
+def with_tiny_norm_rows(inp: Inputs, every: int = 3, factor_log2: int = -10) -> Inputs:
+    """The same document with every `every`-th token row of q and k (all heads,
+    rows 0, every, 2 every, ...) multiplied by 2**factor_log2 (exact in bf16).
+
+    At 2**-10 an N(0, 1) row has mean(x^2) ~ 1e-6, below the RMSNorm epsilon
+    of 1e-5, so these rows make the epsilon (its value and where it enters)
+    visible in the prologue's output; on N(0, 1) rows it changes the result by
+    far less than a bf16 rounding.
+    """
+    rows = np.arange(0, inp.workload.seq_len, every, dtype=np.int64)
+    return Inputs(inp.workload, scale_rows_bf16(inp.q, rows, factor_log2), scale_rows_bf16(inp.k, rows, factor_log2),
+                  inp.v, inp.gamma_q, inp.gamma_k, inp.pos, inp.stress_rows)

@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
 from gates import dgamma_ok, gradient_ok
 from gpu_util import dev_bf16, dev_inputs, host_bits, host_f64
 from packed_full_attention_amd import (h3attn_forward_log2, h3attn_forward_log2_lse, h3attn_qk_prologue_backward_scaled,
@@ -144,12 +145,25 @@ def test_attention_backward_very_negative_scores():
     _compare_attention("very negative scores", q, k, v, (dq, dk, dv), do_bits)
 
 
+def _compare_attention_pooled(tag, q, k, v, grads, do_bits, heads):
+    """As _compare_attention, with the oracle's heads computed in parallel on the host cores."""
+    qf, kf, vf = host_f64(q), host_f64(k), host_f64(v)
+    refs = oracle_pool.attention_backward_heads(qf, kf, vf, _as_f64(do_bits), SCALE, heads)
+    del qf, kf, vf
+    got = [host_f64(t) for t in grads]
+    for h in heads:
+        for name, g, r in zip(("dq", "dk", "dv"), got, refs[h]):
+            _check(f"{tag} head {h} {name}", gradient_ok(g[:, h], r))
+
+
 def test_attention_backward_long_heads(inputs):
-    """L = 16500, H = 56, the whole grid on the GPU; two heads compared in full."""
+    """L = 16500, H = 56, the whole grid on the GPU; compared in full on one head
+    from each run of seven heads (the forward and backward grids give each of
+    the 8 XCDs a contiguous run of about seven heads' work) and the last head."""
     inp = inputs(3)
     q, k, v = _prologue_outputs(inp)
     dq, dk, dv, do_bits = _attention_case(q, k, v, 503)
-    _compare_attention("workload 3", q, k, v, (dq, dk, dv), do_bits, heads=[0, 37])
+    _compare_attention_pooled("workload 3", q, k, v, (dq, dk, dv), do_bits, heads=list(range(0, 56, 7)) + [55])
 
 
 def test_attention_backward_stressed(inputs):
@@ -163,11 +177,11 @@ def test_attention_backward_stressed(inputs):
 
 
 def test_attention_backward_longest(inputs):
-    """L = 28976, H = 7 (one 8-way head share of the 1280x704 video), one head in full."""
+    """L = 28976, H = 7 (one 8-way head share of the 1280x704 video), every head in full."""
     inp = inputs(4)
     q, k, v = _prologue_outputs(inp)
     dq, dk, dv, do_bits = _attention_case(q, k, v, 504)
-    _compare_attention("workload 4", q, k, v, (dq, dk, dv), do_bits, heads=[3])
+    _compare_attention_pooled("workload 4", q, k, v, (dq, dk, dv), do_bits, heads=list(range(7)))
 
 
 def test_attention_backward_deterministic(inputs):
