@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 5
+#define H3ATTN_ABI_VERSION 6
 #define H3ATTN_HEAD_DIM 128
 
 /* Status codes. */
@@ -254,6 +254,26 @@ int h3attn_qk_prologue_backward_scaled(const void* q, const void* k, const float
                                        const float* gamma_k, const int32_t* pos_thw, void* dq, void* dk,
                                        float* dgamma_q, float* dgamma_k, void* workspace, int64_t L,
                                        int32_t H, float q_scale, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate memory -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation -- and so cannot provide the
+ * workspace: h3attn_attention_backward with its per-row statistics held in the
+ * library's own device array (16 MiB on each device that loads the library,
+ * kept until the process ends) instead of a caller workspace.  Same arguments
+ * without the workspace, same kernels, same results bit for bit.
+ *   Limit: H * Lp <= 2^21 (Lp = L rounded up to a multiple of 64; at H = 56,
+ *   L <= 37440); larger (L, H) return H3A_EUNSUPPORTED before any launch.
+ *   `stream` must belong to the calling thread's current device (else
+ *   H3A_EINVAL).  The call allocates nothing; the first call on a device looks
+ *   up that device's array (hipGetSymbolAddress).
+ *   All calls on one device share its array: two of these calls whose work
+ *   overlaps on one device (different streams, no ordering between them) race
+ *   and may give wrong gradients.  Calls ordered on one stream are safe.
+ */
+int h3attn_attention_backward_noalloc(const void* q, const void* k, const void* v, const void* out,
+                                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                      int64_t L, int32_t H, float scale, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* h3attn_strerror(int status);

@@ -23,6 +23,7 @@ EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward", "h3attn_qk_prologue_
                     "h3attn_qk_prologue_backward_workspace_bytes", "h3attn_qk_prologue_backward",
                     "h3attn_rope_table_bytes", "h3attn_k_prologue_table", "h3attn_forward_log2_qprologue",
                     "h3attn_forward_log2_lse", "h3attn_qk_prologue_backward_scaled",
+                    "h3attn_attention_backward_noalloc",
                     "h3attn_strerror", "h3attn_last_error", "h3attn_abi_version")
 
 _lock = threading.Lock()
@@ -78,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.h3attn_forward_log2_lse.restype = ctypes.c_int
         lib.h3attn_qk_prologue_backward_scaled.argtypes = [vp] * 10 + [i64, i32, ctypes.c_float, vp]
         lib.h3attn_qk_prologue_backward_scaled.restype = ctypes.c_int
+        lib.h3attn_attention_backward_noalloc.argtypes = [vp] * 9 + [i64, i32, ctypes.c_float, vp]
+        lib.h3attn_attention_backward_noalloc.restype = ctypes.c_int
         lib.h3attn_strerror.argtypes = [ctypes.c_int]
         lib.h3attn_strerror.restype = ctypes.c_char_p
         lib.h3attn_last_error.argtypes = []
@@ -311,6 +314,27 @@ def h3attn_attention_backward(q, k, v, out, dout, lse, dq=None, dk=None, dv=None
                                            workspace.data_ptr(), L, H, scale,
                                            torch.cuda.current_stream(dev).cuda_stream)
     _raise_on(lib, "h3attn_attention_backward", st)
+    return dq, dk, dv
+
+
+def h3attn_attention_backward_noalloc(q, k, v, out, dout, lse, dq, dk, dv, scale: Optional[float] = None):
+    """h3attn_attention_backward with the statistics in the library's own device
+    array (no workspace, nothing allocated: dq, dk, dv must be given); writes
+    dq, dk, dv and returns them."""
+    import torch
+    L, H = _lh(q)
+    dev = q.device
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    _check_tensor("lse", lse, torch.float32, (H, L), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.h3attn_attention_backward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                   dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                                   dv.data_ptr(), L, H, scale,
+                                                   torch.cuda.current_stream(dev).cuda_stream)
+    _raise_on(lib, "h3attn_attention_backward_noalloc", st)
     return dq, dk, dv
 
 

@@ -45,6 +45,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gfx950_tile.h"
 #include "h3attn_internal.h"
 
@@ -625,6 +627,39 @@ int backward_block_threads() { return kThreads; }
 // One past the last byte a row-tile DMA reads, from the tile's first byte (row
 // kTile - 1, chunk 15); the offsets are 32-bit (see dma_offsets).
 int64_t backward_tile_dma_end(int32_t H) { return (int64_t)(kTile - 1) * H * kD * 2 + kD * 2; }
+
+// ---------------------------------------------------------------- scratch held by the library
+// For callers that cannot allocate: the statistics buffer of the backward
+// ([2][H][Lp] fp32) as a file-scope device array.  Every device that loads the
+// library holds its own copy of kStaticScratchBytes until the process ends.  On
+// the host, `scratch` names a host-side stand-in, not device memory: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is ever handed to a kernel.  All calls on a
+// device share its copy; nothing in it needs clearing, since the dq kernel
+// writes every statistic the dk/dv kernel then reads, in stream order.
+constexpr int64_t kStaticScratchBytes = (int64_t)16 << 20;
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int64_t backward_static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t backward_static_scratch(int dev, float** ptr) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* out, const uint16_t* dout, const float* lse,

@@ -265,10 +265,14 @@ int64_t h3attn_attention_backward_workspace_bytes(int64_t L, int32_t H) {
   return h3attn::backward_workspace_bytes(L, H);
 }
 
-int h3attn_attention_backward(const void* q, const void* k, const void* v, const void* out,
-                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                              void* workspace, int64_t L, int32_t H, float scale, hipStream_t stream) {
-  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace)
+namespace {
+
+// Validation shared by the two forms of the attention backward; workspace may
+// be null for the form that holds its statistics in the library (ws_bytes 0).
+int check_attention_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv, void* workspace, uint64_t ws_bytes,
+                             int64_t L, int32_t H, float scale) {
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || (ws_bytes && !workspace))
     return fail(H3A_EINVAL, "null pointer argument%s");
   uint64_t bytes = 0;
   if (int s = check_shape(L, H, &bytes)) return s;
@@ -277,10 +281,10 @@ int h3attn_attention_backward(const void* q, const void* k, const void* v, const
     if (!aligned(p, 16)) return fail(H3A_EINVAL, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned%s");
   if (!aligned(lse, 4) || !aligned(workspace, 4)) return fail(H3A_EINVAL, "lse and workspace must be 4-byte aligned%s");
   if (!(isfinite(scale) && scale > 0.0f)) return fail(H3A_EINVAL, "scale must be finite and > 0%s");
-  const uint64_t vec = (uint64_t)L * H * 4, ws = (uint64_t)h3attn::backward_workspace_bytes(L, H);
+  const uint64_t vec = (uint64_t)L * H * 4;
   // Written ranges: dq, dk, dv, workspace; none may meet another or any input.
   const void* wr[4] = {dq, dk, dv, workspace};
-  const uint64_t wn[4] = {bytes, bytes, bytes, ws};
+  const uint64_t wn[4] = {bytes, bytes, bytes, ws_bytes};
   const void* in[6] = {q, k, v, out, dout, lse};
   const uint64_t inn[6] = {bytes, bytes, bytes, bytes, bytes, vec};
   for (int i = 0; i < 4; ++i) {
@@ -292,12 +296,50 @@ int h3attn_attention_backward(const void* q, const void* k, const void* v, const
   if (h3attn::backward_grid_blocks(L, H) * h3attn::backward_block_threads() >= kMaxThreadsPerGrid)
     return fail(H3A_EUNSUPPORTED, "backward grid too large for (L, H)%s");
   if (int s = check_row_tiles(H)) return s;
+  return H3A_OK;
+}
+
+int launch_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, float* stats, int64_t L, int32_t H, float scale, hipStream_t stream) {
   const hipError_t e = h3attn::launch_attention_backward(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, static_cast<uint16_t*>(dq),
-      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), static_cast<float*>(workspace), L, H, scale, stream);
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), stats, L, H, scale, stream);
   if (e != hipSuccess) return fail(H3A_EHIP, "backward launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+int h3attn_attention_backward(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              void* workspace, int64_t L, int32_t H, float scale, hipStream_t stream) {
+  uint64_t bytes = 0;
+  const uint64_t ws = check_shape(L, H, &bytes) == H3A_OK ? (uint64_t)h3attn::backward_workspace_bytes(L, H) : 1;
+  if (int s = check_attention_backward(q, k, v, out, dout, lse, dq, dk, dv, workspace, ws, L, H, scale)) return s;
+  return launch_backward(q, k, v, out, dout, lse, dq, dk, dv, static_cast<float*>(workspace), L, H, scale, stream);
+}
+
+int h3attn_attention_backward_noalloc(const void* q, const void* k, const void* v, const void* out,
+                                      const void* dout, const float* lse, void* dq, void* dk, void* dv, int64_t L,
+                                      int32_t H, float scale, hipStream_t stream) {
+  if (int s = check_attention_backward(q, k, v, out, dout, lse, dq, dk, dv, nullptr, 0, L, H, scale)) return s;
+  if (h3attn::backward_workspace_bytes(L, H) > h3attn::backward_static_scratch_bytes())
+    return fail(H3A_EUNSUPPORTED, "(L, H) too large for the library's scratch: needs H * Lp <= 2^21 "
+                                  "(Lp = L rounded up to 64)%s");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(H3A_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (stream != nullptr) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(H3A_EHIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if (sdev != dev) return fail(H3A_EINVAL, "stream belongs to a device other than the current one%s");
+  }
+  float* stats = nullptr;
+  e = h3attn::backward_static_scratch(dev, &stats);
+  if (e != hipSuccess) return fail(H3A_EHIP, "scratch lookup failed: %s", hipGetErrorString(e));
+  return launch_backward(q, k, v, out, dout, lse, dq, dk, dv, stats, L, H, scale, stream);
 }
 
 int64_t h3attn_qk_prologue_backward_workspace_bytes(int64_t L, int32_t H) {

@@ -49,6 +49,13 @@ int64_t backward_workspace_bytes(int64_t L, int32_t H);
 int backward_block_threads();
 int64_t backward_tile_dma_end(int32_t H);
 
+// The library's own statistics buffer for the attention backward, one copy per
+// device, of backward_static_scratch_bytes() bytes: its device address on
+// device dev (which must be the current device; looked up on the first call
+// per device and kept).
+int64_t backward_static_scratch_bytes();
+hipError_t backward_static_scratch(int dev, float** ptr);
+
 // Backward of the prologue (in place on dq, dk) and the gamma gradients;
 // workspace of prologue_backward_workspace_bytes(L) bytes.  q_scale: the
 // factor launch_qk_prologue applied to Q's output (dq is the gradient with

@@ -34,7 +34,7 @@ def test_header_declares_the_expected_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.h3attn_abi_version() == 5
+    assert lib.h3attn_abi_version() == 6
 
 
 def test_strerror_strings(lib):
@@ -246,3 +246,15 @@ def test_prologue_row_count_overflow_rejected(lib):
     }.items():
         assert call() == 2, name
         assert "prologue" in lib.h3attn_last_error().decode(), name
+
+
+def test_noalloc_backward_rejects_before_any_hip_call(lib):
+    # Beyond the library's 16 MiB of statistics (H * Lp <= 2^21): rejected.
+    q, k, v, out, dout, lse, dq, dk, dv = FAR[:9]
+    f = lambda L, H, **kw: lib.h3attn_attention_backward_noalloc(kw.get("q", q), k, v, out, dout, lse, dq, dk, dv,
+                                                                 L, H, kw.get("s", 0.088), None)
+    assert f(37504, 56) == 2 and "scratch" in lib.h3attn_last_error().decode()
+    assert f((1 << 21) + 1, 1) == 2  # Lp = 2^21 + 64 at H = 1 (2^21 itself is the limit)
+    assert f(64, 1, q=None) == 1 and "null" in lib.h3attn_last_error().decode()
+    assert f(0, 1) == 1 and f(64, 1, s=0.0) == 1 and f(64, 1, q=FAR[0] + 8) == 1
+    assert f(64, H_WRAP) == 2
