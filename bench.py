@@ -2,9 +2,9 @@
 over the long single-GPU packed document: L = 16500 tokens (256 text +
 36x15x27 video + 1664 audio), H = 56 heads of 128.
 
-The timed step is the fused, scale-folded form of the path:
-h3attn_k_prologue_table (K's RMSNorm + MM-RoPE in place, and the per-token
-rotation table), h3attn_v_transpose (V^T, a bit-exact copy) and
+The timed step is the fused, scale-folded form of the path, two launches:
+h3attn_kv_prologue (K's RMSNorm + MM-RoPE in place, the per-token rotation
+table and V^T, a bit-exact copy of V transposed) and
 h3attn_forward_log2_qprologue (base-2 softmax on V^T, with Q's RMSNorm +
 MM-RoPE and the factor scale * log2(e) applied at the kernel's Q load).  Its
 output is bit-identical to the unfused h3attn_qk_prologue_scaled +
@@ -19,8 +19,13 @@ Prints one JSON line.  `value` is attention TFLOP/s (4 L^2 128 H per step)
 over the whole step's time; the `roofline` object prices the attention kernel
 alone (HIP events around each launch on the stream it runs on) against the
 dense bf16 matrix-core peak; `prologue` prices the standalone Q/K prologue
-kernel (of the unfused path) and `k_prologue` the K-only one against HBM peak; `cpu_baseline` is the fp64 oracle on a bounded sample, timed on
-this host's cores.  Inputs are generated, copied to the GPU and resident in
+kernel (of the unfused path) and `kv_prologue` the step's K-prologue + V^T
+kernel against HBM peak; `cpu_baseline` is the fp64 oracle on a bounded
+sample, timed on this host's cores.  The roofline's `traffic`,
+`mfma_busy_pct` and `sclk_mhz` are not measured by this run: they are read
+from the committed counter summaries under profiles/ (named in
+`counters_from`) and given only while those were taken on the current kernel
+source.  Inputs are generated, copied to the GPU and resident in
 HBM before the timed region starts.
 """
 from __future__ import annotations
@@ -55,9 +60,10 @@ def prologue_bytes(L: int, H: int) -> float:
     return 8.0 * L * H * 128 + 12.0 * L + 1024.0
 
 
-def k_prologue_bytes(L: int, H: int) -> float:
-    # read + write of K, the 384 B/token rotation table written, positions, gamma_k
-    return 4.0 * L * H * 128 + 384.0 * L + 12.0 * L + 512.0
+def kv_prologue_bytes(L: int, H: int) -> float:
+    # K read + written, V read, V^T written (2 B each per element), the 384 B/token
+    # rotation table written, 12 B/token positions, gamma_k
+    return 8.0 * L * H * 128 + 384.0 * L + 12.0 * L + 512.0
 
 
 def kernel_source_sha() -> str:
@@ -146,7 +152,7 @@ def main() -> int:
     import torch
     from packed_full_attention_amd import (h3attn_attention_backward, h3attn_forward, h3attn_forward_log2,
                                            h3attn_forward_log2_lse, h3attn_forward_log2_qprologue,
-                                           h3attn_k_prologue_table, h3attn_qk_prologue, h3attn_qk_prologue_backward_scaled,
+                                           h3attn_kv_prologue, h3attn_qk_prologue, h3attn_qk_prologue_backward_scaled,
                                            h3attn_qk_prologue_scaled, h3attn_v_transpose, load_library)
     from packed_full_attention_amd import workloads as wl
 
@@ -211,8 +217,7 @@ def main() -> int:
             b.copy_(k)
         torch.cuda.synchronize()
 
-    fused = [lambda i: h3attn_k_prologue_table(ks[i], gk, pos, rope_cs),
-             lambda i: h3attn_v_transpose(v, vt),
+    fused = [lambda i: h3attn_kv_prologue(ks[i], v, gk, pos, rope_cs, vt),
              lambda i: h3attn_forward_log2_qprologue(qs[i], ks[i], vt, gq, rope_cs, q_scale, out)]
     fast = [lambda i: h3attn_qk_prologue_scaled(qs[i], ks[i], gq, gk, pos, q_scale),
             lambda i: h3attn_v_transpose(v, vt),
@@ -234,7 +239,7 @@ def main() -> int:
     for i in range(W):
         for f in fused:
             f(i)
-    ms_step, (t_kpro, t_vt, t_att), wall_ms = timed(fused, K, W)
+    ms_step, (t_kv, t_att), wall_ms = timed(fused, K, W)
     del qs, ks
 
     # Training pieces, timed separately (not part of `value`), in the scale-folded
@@ -283,7 +288,7 @@ def main() -> int:
     flops = attention_flops(L, H)
     att_tflops = flops / (t_att * 1e-3) / 1e12
     pro_gbs = prologue_bytes(L, H) / (t_pro * 1e-3) / 1e9
-    kpro_gbs = k_prologue_bytes(L, H) / (t_kpro * 1e-3) / 1e9
+    kv_gbs = kv_prologue_bytes(L, H) / (t_kv * 1e-3) / 1e9
     traffic = measured_traffic(L, H)
     mfma_busy, sclk = measured_mfma(L, H)
     result = {
@@ -306,20 +311,21 @@ def main() -> int:
                      "achieved": round(att_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "avg_launch_ms": round(t_att, 4), "mfma_busy_pct": mfma_busy, "sclk_mhz": sclk},
+                     "avg_launch_ms": round(t_att, 4), "mfma_busy_pct": mfma_busy, "sclk_mhz": sclk,
+                     "counters_from": [f"profiles/attention_fwd_L{L}_H{H}_traffic.md",
+                                       f"profiles/attention_fwd_L{L}_H{H}_mfma_util.md"],
+                     "counters_measured_in_this_run": False},
         "prologue": {"bound": "hbm", "kernel": "qk_prologue_kernel", "achieved": round(pro_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(pro_gbs / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes": prologue_bytes(L, H), "avg_launch_us": round(t_pro * 1e3, 2),
                      "copy_reference_gbs": round(copy_gbs, 1), "frac_of_copy": round(pro_gbs / copy_gbs, 4)},
-        "k_prologue": {"bound": "hbm", "kernel": "qk_prologue_kernel<K only>", "achieved": round(kpro_gbs, 1),
-                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kpro_gbs / PEAK_HBM_GBS, 4),
-                       "algorithmic_bytes": k_prologue_bytes(L, H), "avg_launch_us": round(t_kpro * 1e3, 2)},
+        "kv_prologue": {"bound": "hbm", "kernel": "kv_prologue_kernel", "achieved": round(kv_gbs, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kv_gbs / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes": kv_prologue_bytes(L, H), "avg_launch_us": round(t_kv * 1e3, 2)},
         "scale_folded_path": {"entry_points": "h3attn_qk_prologue_scaled + h3attn_v_transpose + h3attn_forward_log2",
                               "ms_per_step": round(fast_ms, 4), "attention_ms": round(t_att_fast, 4),
                               "attention_tflops": round(flops / (t_att_fast * 1e-3) / 1e12, 2),
                               "v_transpose_us": round(t_vt_fast * 1e3, 2)},
-        "v_transpose": {"bound": "hbm", "kernel": "v_transpose_kernel", "avg_launch_us": round(t_vt * 1e3, 2),
-                        "achieved": round(2.0 * L * H * 128 * 2 / (t_vt * 1e-3) / 1e9, 1), "unit": "GB/s"},
         "plain_path": {"entry_points": "h3attn_qk_prologue + h3attn_forward", "ms_per_step": round(plain_ms, 4),
                        "attention_ms": round(plain_att, 4),
                        "attention_tflops": round(flops / (plain_att * 1e-3) / 1e12, 2),

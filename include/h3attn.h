@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 6
+#define H3ATTN_ABI_VERSION 7
 #define H3ATTN_HEAD_DIM 128
 
 /* Status codes. */
@@ -173,6 +173,18 @@ int h3attn_forward_log2(const void* q, const void* k, const void* vt, void* out,
  *   aligned; q_scale finite and > 0 (scale * log2(e) for softmax scale
  *   `scale`); out must not overlap q, k, vt, gamma_q or rope_cs.
  */
+/*
+ * h3attn_kv_prologue: h3attn_k_prologue_table(k, gamma_k, pos_thw, rope_cs, L, H, s)
+ *   and h3attn_v_transpose(v, vt, L, H, s) in one launch, with the same results
+ *   bit for bit (k rewritten in place, rope_cs fp32 [L][96], vt bf16
+ *   [H][128][Lp]): the two memory-bound passes the fused attention call needs,
+ *   their traffic spread over one grid.  k, v, rope_cs, vt 16-byte aligned;
+ *   gamma_k, pos_thw 4-byte aligned; k, rope_cs and vt must not overlap one
+ *   another or v, gamma_k, pos_thw.
+ */
+int h3attn_kv_prologue(void* k, const void* v, const float* gamma_k, const int32_t* pos_thw, float* rope_cs,
+                       void* vt, int64_t L, int32_t H, hipStream_t stream);
+
 int64_t h3attn_rope_table_bytes(int64_t L, int32_t H);
 int h3attn_k_prologue_table(void* k, const float* gamma_k, const int32_t* pos_thw, float* rope_cs,
                             int64_t L, int32_t H, hipStream_t stream);

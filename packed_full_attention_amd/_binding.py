@@ -23,7 +23,7 @@ EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward", "h3attn_qk_prologue_
                     "h3attn_qk_prologue_backward_workspace_bytes", "h3attn_qk_prologue_backward",
                     "h3attn_rope_table_bytes", "h3attn_k_prologue_table", "h3attn_forward_log2_qprologue",
                     "h3attn_forward_log2_lse", "h3attn_qk_prologue_backward_scaled",
-                    "h3attn_attention_backward_noalloc",
+                    "h3attn_attention_backward_noalloc", "h3attn_kv_prologue",
                     "h3attn_strerror", "h3attn_last_error", "h3attn_abi_version")
 
 _lock = threading.Lock()
@@ -81,6 +81,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.h3attn_qk_prologue_backward_scaled.restype = ctypes.c_int
         lib.h3attn_attention_backward_noalloc.argtypes = [vp] * 9 + [i64, i32, ctypes.c_float, vp]
         lib.h3attn_attention_backward_noalloc.restype = ctypes.c_int
+        lib.h3attn_kv_prologue.argtypes = [vp] * 6 + [i64, i32, vp]
+        lib.h3attn_kv_prologue.restype = ctypes.c_int
         lib.h3attn_strerror.argtypes = [ctypes.c_int]
         lib.h3attn_strerror.restype = ctypes.c_char_p
         lib.h3attn_last_error.argtypes = []
@@ -226,6 +228,30 @@ def h3attn_k_prologue_table(k, gamma_k, pos_thw, rope_cs=None):
                                          L, H, torch.cuda.current_stream(dev).cuda_stream)
     _raise_on(lib, "h3attn_k_prologue_table", st)
     return rope_cs
+
+
+def h3attn_kv_prologue(k, v, gamma_k, pos_thw, rope_cs=None, vt=None):
+    """h3attn_k_prologue_table and h3attn_v_transpose in one launch: k rewritten in place,
+    returns (rope_cs fp32 [L, 96], vt bf16 [H, 128, Lp])."""
+    import torch
+    L, H = _lh(k)
+    dev = k.device
+    _check_tensor("k", k, torch.bfloat16, (L, H, HEAD_DIM))
+    _check_tensor("v", v, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    _check_tensor("gamma_k", gamma_k, torch.float32, (HEAD_DIM,), dev)
+    _check_tensor("pos_thw", pos_thw, torch.int32, (L, 3), dev)
+    if rope_cs is None:
+        rope_cs = torch.empty(L, 96, dtype=torch.float32, device=dev)
+    if vt is None:
+        vt = torch.empty(H, HEAD_DIM, padded_length(L), dtype=torch.bfloat16, device=dev)
+    _check_tensor("rope_cs", rope_cs, torch.float32, (L, 96), dev)
+    _check_tensor("vt", vt, torch.bfloat16, (H, HEAD_DIM, padded_length(L)), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.h3attn_kv_prologue(k.data_ptr(), v.data_ptr(), gamma_k.data_ptr(), pos_thw.data_ptr(),
+                                    rope_cs.data_ptr(), vt.data_ptr(), L, H, torch.cuda.current_stream(dev).cuda_stream)
+    _raise_on(lib, "h3attn_kv_prologue", st)
+    return rope_cs, vt
 
 
 def h3attn_forward_log2_qprologue(q, k, vt, gamma_q, rope_cs, q_scale: float, out=None):

@@ -748,48 +748,6 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   }
 }
 
-// ---------------------------------------------------------------- V transpose
-// vt[h][c][j] = v[j][h][c] for j < L, 0 for L <= j < Lp (Lp = L rounded up
-// to 64): the layout the log2 attention variant reads V in.  One 256-thread
-// workgroup per (64-key block, head): the block's 64 rows x 256 bytes go
-// through LDS (row stride 65 words: the column reads then hit 32 distinct
-// banks), and every 8 consecutive lanes write one 128-byte run of a V^T row.
-constexpr int kVtThreads = 256;
-
-__global__ __launch_bounds__(kVtThreads) void v_transpose_kernel(const uint16_t* __restrict__ v,
-                                                                 uint16_t* __restrict__ vt, int L, int H,
-                                                                 int Lp) {
-  __shared__ uint32_t tile[kBN * 65];
-  const int nblk = Lp / kBN;
-  const int head = blockIdx.x / nblk, key0 = (blockIdx.x - head * nblk) * kBN, tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = i * kVtThreads + tid, r = idx >> 4, c16 = idx & 15;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (key0 + r < L)
-      val = *reinterpret_cast<const uint4*>(v + ((int64_t)(key0 + r) * H + head) * kD + 8 * c16);
-    uint32_t* dst = tile + r * 65 + 4 * c16;
-    dst[0] = val.x;
-    dst[1] = val.y;
-    dst[2] = val.z;
-    dst[3] = val.w;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = i * kVtThreads + tid, d = idx >> 3, c = idx & 7;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = tile[(8 * c + 2 * e) * 65 + (d >> 1)];
-      const uint32_t hi = tile[(8 * c + 2 * e + 1) * 65 + (d >> 1)];
-      w[e] = (d & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    *reinterpret_cast<uint4*>(vt + ((int64_t)head * kD + d) * Lp + key0 + 8 * c) =
-        make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 }  // namespace
 
 int64_t attention_grid_blocks(int64_t L, int32_t H) { return ((L + kBM - 1) / kBM) * (int64_t)H; }
@@ -804,15 +762,6 @@ int64_t vt_tile_dma_end(int64_t L) { return (int64_t)(kD - 1) * vt_padded_length
 
 int64_t vt_padded_length(int64_t L) { return (L + kBN - 1) / kBN * kBN; }
 int64_t vt_bytes(int64_t L, int32_t H) { return (int64_t)H * kD * vt_padded_length(L) * 2; }
-int64_t transpose_grid_blocks(int64_t L, int32_t H) { return vt_padded_length(L) / kBN * (int64_t)H; }
-int transpose_block_threads() { return kVtThreads; }
-
-hipError_t launch_v_transpose(const uint16_t* v, uint16_t* vt, int64_t L, int32_t H, hipStream_t stream) {
-  hipLaunchKernelGGL(v_transpose_kernel, dim3((unsigned)transpose_grid_blocks(L, H)), dim3(kVtThreads), 0,
-                     stream, v, vt, (int)L, (int)H, (int)vt_padded_length(L));
-  return hipGetLastError();
-}
-
 hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                     uint16_t* out, float* lse, int64_t L, int32_t H, float scale, bool log2,
                                     hipStream_t stream) {

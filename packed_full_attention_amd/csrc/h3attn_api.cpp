@@ -234,6 +234,36 @@ int h3attn_k_prologue_table(void* k, const float* gamma_k, const int32_t* pos_th
   return ok();
 }
 
+int h3attn_kv_prologue(void* k, const void* v, const float* gamma_k, const int32_t* pos_thw, float* rope_cs, void* vt,
+                       int64_t L, int32_t H, hipStream_t stream) {
+  if (!k || !v || !gamma_k || !pos_thw || !rope_cs || !vt) return fail(H3A_EINVAL, "null pointer argument%s");
+  uint64_t bytes = 0;
+  if (int s = check_shape(L, H, &bytes)) return s;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(rope_cs, 16) || !aligned(vt, 16))
+    return fail(H3A_EINVAL, "k, v, rope_cs and vt must be 16-byte aligned%s");
+  if (!aligned(gamma_k, 4) || !aligned(pos_thw, 4))
+    return fail(H3A_EINVAL, "gamma_k and pos_thw must be 4-byte aligned%s");
+  // Written: k (in place), rope_cs, vt; read: v, gamma_k, pos_thw (and k).
+  const uint64_t tbytes = (uint64_t)L * 96 * 4, vtb = (uint64_t)h3attn::vt_bytes(L, H), pbytes = (uint64_t)L * 12;
+  const void* wr[3] = {k, rope_cs, vt};
+  const uint64_t wn[3] = {bytes, tbytes, vtb};
+  const void* in[3] = {v, gamma_k, pos_thw};
+  const uint64_t inn[3] = {bytes, 512, pbytes};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlap(wr[i], wn[i], in[j], inn[j])) return fail(H3A_EINVAL, "k, rope_cs or vt overlaps v, gamma_k or pos_thw%s");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(wr[i], wn[i], wr[j], wn[j])) return fail(H3A_EINVAL, "k, rope_cs and vt overlap%s");
+  }
+  if (h3attn::kv_prologue_grid_blocks(L, H) * h3attn::transpose_block_threads() >= kMaxThreadsPerGrid)
+    return fail(H3A_EUNSUPPORTED, "prologue grid too large for (L, H)%s");
+  if (int s = check_prologue_rows(H)) return s;
+  const hipError_t e = h3attn::launch_kv_prologue(static_cast<uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                                  static_cast<uint16_t*>(vt), gamma_k, pos_thw, rope_cs, L, H, stream);
+  if (e != hipSuccess) return fail(H3A_EHIP, "prologue launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int h3attn_forward_log2_qprologue(const void* q, const void* k, const void* vt, void* out, const float* gamma_q,
                                   const float* rope_cs, int64_t L, int32_t H, float q_scale, hipStream_t stream) {
   if (!q || !k || !vt || !out || !gamma_q || !rope_cs) return fail(H3A_EINVAL, "null pointer argument%s");

@@ -68,6 +68,12 @@ int64_t prologue_backward_workspace_bytes(int64_t L);
 
 // V^T = [H][128][Lp] bf16, Lp = L rounded up to 64, zeros past L.
 hipError_t launch_v_transpose(const uint16_t* v, uint16_t* vt, int64_t L, int32_t H, hipStream_t stream);
+
+// launch_k_prologue and launch_v_transpose in one launch (same results, bit
+// for bit); its grid size for validation.
+hipError_t launch_kv_prologue(uint16_t* k, const uint16_t* v, uint16_t* vt, const float* gamma_k, const int32_t* pos,
+                              float* rope_cs, int64_t L, int32_t H, hipStream_t stream);
+int64_t kv_prologue_grid_blocks(int64_t L, int32_t H);
 int64_t vt_padded_length(int64_t L);
 int64_t vt_bytes(int64_t L, int32_t H);
 int64_t transpose_grid_blocks(int64_t L, int32_t H);

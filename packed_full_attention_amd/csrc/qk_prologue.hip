@@ -50,18 +50,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// kKOnly: only K's rows, and the lane's cosines and sines go to rope_cs
-// (fp32 [L][96]: cos of the token's 48 angles, then their sines) for an
-// attention kernel that applies Q's prologue itself.
+// One wave's work: every head row of one token (Q's, then K's).  kKOnly:
+// only K's rows, and the lane's cosines and sines go to rope_cs (fp32 [L][96]:
+// cos of the token's 48 angles, then their sines) for an attention kernel that
+// applies Q's prologue itself.
 template <int kPassesPerChunk, bool kKOnly>
-__global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
-    uint16_t* __restrict__ q, uint16_t* __restrict__ k, const float* __restrict__ gamma_q,
-    const float* __restrict__ gamma_k, const int32_t* __restrict__ pos, int64_t L, int32_t H,
-    float q_scale, float* __restrict__ rope_cs) {
-  const int lane = threadIdx.x & 63;
-  const int64_t token = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (token >= L) return;  // whole wave exits together
-
+__device__ __forceinline__ void prologue_token(uint16_t* __restrict__ q, uint16_t* __restrict__ k,
+                                               const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
+                                               const int32_t* __restrict__ pos, int64_t token, int32_t H,
+                                               float q_scale, float* __restrict__ rope_cs, int lane) {
   const int sub = lane >> 4;  // which of the pass's 4 rows this quarter-wave owns
   const int i = lane & 15;    // lane within the row
   const bool pair_lane = i < 12;
@@ -142,6 +139,98 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
       }
     }
   }
+}
+
+template <int kPassesPerChunk, bool kKOnly>
+__global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_kernel(
+    uint16_t* __restrict__ q, uint16_t* __restrict__ k, const float* __restrict__ gamma_q,
+    const float* __restrict__ gamma_k, const int32_t* __restrict__ pos, int64_t L, int32_t H,
+    float q_scale, float* __restrict__ rope_cs) {
+  const int64_t token = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (token >= L) return;  // whole wave exits together
+  prologue_token<kPassesPerChunk, kKOnly>(q, k, gamma_q, gamma_k, pos, token, H, q_scale, rope_cs,
+                                          threadIdx.x & 63);
+}
+
+// ---------------------------------------------------------------- V transpose
+// vt[h][c][j] = v[j][h][c] for j < L, 0 for L <= j < Lp (Lp = L rounded up
+// to 64): the layout the log2 attention kernels read V in.  One 256-thread
+// workgroup per (64-key block, head): the block's 64 rows x 256 bytes go
+// through LDS (row stride 65 words: the column reads then hit 32 distinct
+// banks), and every 8 consecutive lanes write one 128-byte run of a V^T row.
+constexpr int kVtThreads = 256;
+constexpr int kVtKeys = 64;
+constexpr int kVtTileWords = kVtKeys * 65;
+
+__device__ __forceinline__ void v_transpose_tile(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt, int L,
+                                                 int H, int Lp, int head, int key0, int tid, uint32_t* tile) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * kVtThreads + tid, r = idx >> 4, c16 = idx & 15;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (key0 + r < L)
+      val = *reinterpret_cast<const uint4*>(v + ((int64_t)(key0 + r) * H + head) * kHeadDim + 8 * c16);
+    uint32_t* dst = tile + r * 65 + 4 * c16;
+    dst[0] = val.x;
+    dst[1] = val.y;
+    dst[2] = val.z;
+    dst[3] = val.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = i * kVtThreads + tid, d = idx >> 3, c = idx & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = tile[(8 * c + 2 * e) * 65 + (d >> 1)];
+      const uint32_t hi = tile[(8 * c + 2 * e + 1) * 65 + (d >> 1)];
+      w[e] = (d & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    *reinterpret_cast<uint4*>(vt + ((int64_t)head * kHeadDim + d) * Lp + key0 + 8 * c) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+__global__ __launch_bounds__(kVtThreads) void v_transpose_kernel(const uint16_t* __restrict__ v,
+                                                                 uint16_t* __restrict__ vt, int L, int H,
+                                                                 int Lp) {
+  __shared__ uint32_t tile[kVtTileWords];
+  const int nblk = Lp / kVtKeys;
+  const int head = blockIdx.x / nblk, key0 = (blockIdx.x - head * nblk) * kVtKeys;
+  v_transpose_tile(v, vt, L, H, Lp, head, key0, threadIdx.x, tile);
+}
+
+// ---------------------------------------------------------------- K prologue + V transpose
+// One launch for the two passes the attention kernel with Q's prologue at its
+// load needs before it runs: K's prologue in place with the rotation table
+// (prologue_token, K only: the same bits as qk_prologue_kernel<P, true>) and
+// V^T (v_transpose_tile: the same bits as v_transpose_kernel).  The two kinds
+// of workgroup are dealt out in proportion, evenly over the grid (workgroup b
+// does K work when floor((b + 1) nk / n) > floor(b nk / n)), so K's in-place
+// traffic and V's read-and-scatter traffic share the memory system for the
+// whole launch instead of running one after the other.
+static_assert(kWavesPerBlock * 64 == kVtThreads, "both kinds of workgroup have 256 threads");
+
+template <int kPassesPerChunk>
+__global__ __launch_bounds__(kVtThreads) void kv_prologue_kernel(
+    uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ vt,
+    const float* __restrict__ gamma_k, const int32_t* __restrict__ pos, float* __restrict__ rope_cs, int64_t L,
+    int32_t H, int Lp, int64_t nk, int64_t n) {
+  __shared__ uint32_t tile[kVtTileWords];
+  const int64_t b = blockIdx.x;
+  const int64_t kb = b * nk / n;
+  if ((b + 1) * nk / n > kb) {
+    const int64_t token = kb * kWavesPerBlock + (threadIdx.x >> 6);
+    if (token < L)
+      prologue_token<kPassesPerChunk, true>(nullptr, k, gamma_k, gamma_k, pos, token, H, 1.0f, rope_cs,
+                                            threadIdx.x & 63);
+    return;
+  }
+  const int64_t vb = b - kb;  // V workgroups before this one
+  const int nblk = Lp / kVtKeys;
+  const int head = (int)(vb / nblk), key0 = (int)(vb - (int64_t)head * nblk) * kVtKeys;
+  v_transpose_tile(v, vt, (int)L, H, Lp, head, key0, threadIdx.x, tile);
 }
 
 // ---------------------------------------------------------------- backward
@@ -348,6 +437,16 @@ static int prologue_passes(int64_t n) {
   return best;
 }
 
+int64_t transpose_grid_blocks(int64_t L, int32_t H) { return vt_padded_length(L) / kVtKeys * (int64_t)H; }
+int transpose_block_threads() { return kVtThreads; }
+int64_t kv_prologue_grid_blocks(int64_t L, int32_t H) { return prologue_grid_blocks(L) + transpose_grid_blocks(L, H); }
+
+hipError_t launch_v_transpose(const uint16_t* v, uint16_t* vt, int64_t L, int32_t H, hipStream_t stream) {
+  hipLaunchKernelGGL(v_transpose_kernel, dim3((unsigned)transpose_grid_blocks(L, H)), dim3(kVtThreads), 0,
+                     stream, v, vt, (int)L, (int)H, (int)vt_padded_length(L));
+  return hipGetLastError();
+}
+
 template <bool kKOnly>
 static void launch_prologue(uint16_t* q, uint16_t* k, const float* gamma_q, const float* gamma_k,
                             const int32_t* pos, int64_t L, int32_t H, float q_scale, float* rope_cs,
@@ -378,6 +477,28 @@ hipError_t launch_qk_prologue(uint16_t* q, uint16_t* k, const float* gamma_q, co
 hipError_t launch_k_prologue(uint16_t* k, const float* gamma_k, const int32_t* pos, float* rope_cs, int64_t L,
                              int32_t H, hipStream_t stream) {
   launch_prologue<true>(nullptr, k, gamma_k, gamma_k, pos, L, H, 1.0f, rope_cs, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_prologue(uint16_t* k, const uint16_t* v, uint16_t* vt, const float* gamma_k, const int32_t* pos,
+                              float* rope_cs, int64_t L, int32_t H, hipStream_t stream) {
+  const int64_t nk = prologue_grid_blocks(L), n = kv_prologue_grid_blocks(L, H);
+  const int Lp = (int)vt_padded_length(L);
+  const dim3 grid((unsigned)n), block(kVtThreads);
+  switch (prologue_passes(H)) {
+    case 14:
+      hipLaunchKernelGGL(kv_prologue_kernel<14>, grid, block, 0, stream, k, v, vt, gamma_k, pos, rope_cs, L, H, Lp,
+                         nk, n);
+      break;
+    case 8:
+      hipLaunchKernelGGL(kv_prologue_kernel<8>, grid, block, 0, stream, k, v, vt, gamma_k, pos, rope_cs, L, H, Lp,
+                         nk, n);
+      break;
+    default:
+      hipLaunchKernelGGL(kv_prologue_kernel<4>, grid, block, 0, stream, k, v, vt, gamma_k, pos, rope_cs, L, H, Lp,
+                         nk, n);
+      break;
+  }
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ import oracle
 from gates import attention_ok
 from gpu_util import dev_bf16, dev_inputs, host_bits, host_f64
 from packed_full_attention_amd import (h3attn_forward_log2, h3attn_forward_log2_qprologue, h3attn_k_prologue_table,
-                                       h3attn_qk_prologue_scaled, h3attn_v_transpose)
+                                       h3attn_kv_prologue, h3attn_qk_prologue_scaled, h3attn_v_transpose)
 from packed_full_attention_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -145,3 +145,65 @@ def test_k_prologue_table_writes_only_its_buffers():
     assert not np.any(np.isnan(th[guard:guard + L * 96]))
     out_u, k_u = unfused(inp)
     assert np.array_equal(kh[guard:guard + n].reshape(L, H, 128), k_u)
+
+
+# ------------------------------------------------------------------ h3attn_kv_prologue
+
+def _kv_pair(inp):
+    """(k', rope_cs, vt) from h3attn_k_prologue_table + h3attn_v_transpose and from
+    h3attn_kv_prologue, on the same inputs."""
+    _, k1, v, _, gk, pos = dev_inputs(inp)
+    cs1 = h3attn_k_prologue_table(k1, gk, pos)
+    vt1 = h3attn_v_transpose(v)
+    k2 = dev_bf16(inp.k)
+    cs2, vt2 = h3attn_kv_prologue(k2, v, gk, pos)
+    torch.cuda.synchronize()
+    return (host_bits(k1), cs1.cpu().numpy(), host_bits(vt1)), (host_bits(k2), cs2.cpu().numpy(), host_bits(vt2))
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_kv_prologue_bit_identical_to_the_two_passes(idx):
+    inp = with_stress(wl.make_inputs(idx))
+    print(f"kv prologue vs two passes, workload {idx}: {inp.workload.describe()}", flush=True)
+    (k1, cs1, vt1), (k2, cs2, vt2) = _kv_pair(inp)
+    assert np.array_equal(k1, k2)
+    assert np.array_equal(cs1.view(np.uint32), cs2.view(np.uint32))
+    assert np.array_equal(vt1, vt2)
+
+
+@pytest.mark.parametrize("L,H", [(1, 1), (2, 3), (63, 2), (64, 1), (65, 3), (255, 1), (257, 2), (1000, 5),
+                                 (777, 57)])
+def test_kv_prologue_bit_identical_edge_lengths(L, H):
+    inp = wl.random_document(L, H, seed=700 + L + H, pos_max=5000)
+    print(f"kv prologue vs two passes, L={L} H={H}", flush=True)
+    (k1, cs1, vt1), (k2, cs2, vt2) = _kv_pair(inp)
+    assert np.array_equal(k1, k2) and np.array_equal(vt1, vt2)
+    assert np.array_equal(cs1.view(np.uint32), cs2.view(np.uint32))
+    # V^T is an exact copy with zero padding.
+    Lp = (L + 63) // 64 * 64
+    want = np.zeros((H, 128, Lp), np.uint16)
+    want[:, :, :L] = inp.v.transpose(1, 2, 0)
+    assert np.array_equal(vt2, want)
+
+
+def test_kv_prologue_writes_only_its_buffers():
+    L, H = 130, 3
+    inp = wl.random_document(L, H, seed=29)
+    n, guard, Lp = L * H * 128, 4096, 192
+    kfull = dev_bf16(np.full(n + 2 * guard, 0x7FC1, np.uint16))
+    k = kfull[guard:guard + n].view(L, H, 128)
+    k.copy_(dev_bf16(inp.k))
+    tfull = torch.full((L * 96 + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda")
+    cs = tfull[guard:guard + L * 96].view(L, 96)
+    nv = H * 128 * Lp
+    vfull = dev_bf16(np.full(nv + 2 * guard, 0x7FC1, np.uint16))
+    vt = vfull[guard:guard + nv].view(H, 128, Lp)
+    _, _, v, _, gk, pos = dev_inputs(inp)
+    h3attn_kv_prologue(k, v, gk, pos, cs, vt)
+    torch.cuda.synchronize()
+    kh, th, vh = host_bits(kfull), tfull.cpu().numpy(), host_bits(vfull)
+    for a in (kh, vh):
+        assert np.all(a[:guard] == 0x7FC1) and np.all(a[-guard:] == 0x7FC1)
+    assert np.all(np.isnan(th[:guard])) and np.all(np.isnan(th[-guard:]))
+    assert not np.any(np.isnan(th[guard:guard + L * 96]))
+    assert not np.any(vh[guard:guard + nv] == 0x7FC1)

@@ -8,8 +8,9 @@ h3_qk_rmsnorm_d128, h3_mm_rope_3axis_partial, h3_full_attention):
   plain         h3attn_qk_prologue + h3attn_forward
   scale-folded  h3attn_qk_prologue_scaled (q' carries scale log2 e) +
                 h3attn_v_transpose + h3attn_forward_log2
-  fused         h3attn_k_prologue_table + h3attn_v_transpose +
-                h3attn_forward_log2_qprologue (Q's prologue inside attention)
+  fused         h3attn_kv_prologue (K's prologue, the rotation table and V^T
+                in one launch) + h3attn_forward_log2_qprologue (Q's prologue
+                inside attention), the form the benchmark times
 Gates (tests/gates.py): attention output max-abs <= 2e-2, mean-abs <= 2e-3 and
 rel-L2 <= 1e-2 over all outputs; the prologue outputs that leave the GPU (Q'
 and K', or K' alone for the fused form) |gpu - ref| <= 2^-8 (|ref| + 1) per
@@ -27,7 +28,7 @@ import oracle_pool
 from gates import attention_ok, prologue_ok
 from gpu_util import dev_bf16, dev_inputs, host_f64
 from packed_full_attention_amd import (h3attn_forward, h3attn_forward_log2, h3attn_forward_log2_qprologue,
-                                       h3attn_k_prologue_table, h3attn_qk_prologue, h3attn_qk_prologue_scaled,
+                                       h3attn_kv_prologue, h3attn_qk_prologue, h3attn_qk_prologue_scaled,
                                        h3attn_v_transpose)
 from packed_full_attention_amd import workloads as wl
 
@@ -78,8 +79,8 @@ def test_path_parity_full(reference, idx, path):
         out = h3attn_forward_log2(q, k, h3attn_v_transpose(v))
         checks = (("q' (scaled)", q, qr * Q_SCALE), ("k'", k, kr))
     else:
-        cs = h3attn_k_prologue_table(k, gk, pos)
-        out = h3attn_forward_log2_qprologue(q, k, h3attn_v_transpose(v), gq, cs, Q_SCALE)
+        cs, vt = h3attn_kv_prologue(k, v, gk, pos)
+        out = h3attn_forward_log2_qprologue(q, k, vt, gq, cs, Q_SCALE)
         checks = (("k'", k, kr),)
     torch.cuda.synchronize()
     for name, got, want in checks:
