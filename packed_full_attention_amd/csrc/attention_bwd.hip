@@ -415,7 +415,7 @@ constexpr int kFusedStages = 4;
 constexpr int kFusedWaves = 4;
 constexpr int kFusedRows = 32 * kFusedWaves;
 constexpr int kFusedPieces = 2 * dma_per_wave<kFusedWaves>();  // Q and dO pieces per wave per tile
-constexpr int kAhead = 2;                                       // operand reads this many slots early
+constexpr int kAhead = 4;                                       // operand reads this many slots early
 
 // dK and dV in one pass over the queries (S computed once per tile): a
 // workgroup of 4 waves, one per SIMD, owning 128 keys.  One wave per SIMD has

@@ -42,6 +42,34 @@ constexpr int kWavesPerBlock = 4;     // one token per wave
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// x from lane (lane ^ m) of the same 16-lane row, m in {1, 2, 4, 8}, through
+// the data-parallel-primitive lane selects of the vector ALU (no LDS round
+// trip): quad permutes for m = 1, 2; a rotation by 8 within the row for m = 8;
+// and for m = 4, a shift left by 4 into lane groups 0-3 and 8-11 and a shift
+// right by 4 into lane groups 4-7 and 12-15 (the bank mask picks the groups).
+template <int m>
+__device__ __forceinline__ float row_xor(float x) {
+  const int v = __float_as_int(x);
+  int r;
+  if (m == 1) r = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);        // quad_perm [1,0,3,2]
+  else if (m == 2) r = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  else if (m == 8) r = __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  else {
+    r = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0x5, false);   // row_shl:4 into groups 0, 2
+    r = __builtin_amdgcn_update_dpp(r, v, 0x114, 0xF, 0xA, false);   // row_shr:4 into groups 1, 3
+  }
+  return __int_as_float(r);
+}
+
+// The sum over the 16 lanes of a row by the xor butterfly (1, 2, 4, 8): every
+// lane ends with the same bits.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += row_xor<1>(x);
+  x += row_xor<2>(x);
+  x += row_xor<4>(x);
+  return x + row_xor<8>(x);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x2_t r;
@@ -118,10 +146,7 @@ __device__ __forceinline__ void prologue_token(uint16_t* __restrict__ q, uint16_
 #pragma unroll
       for (int e = 0; e < 4; ++e) ss = fmaf(xb[e], xb[e], ss);
       // Butterfly over the 16 lanes of the row: every lane ends with the same sum.
-      ss += __shfl_xor(ss, 1, 16);
-      ss += __shfl_xor(ss, 2, 16);
-      ss += __shfl_xor(ss, 4, 16);
-      ss += __shfl_xor(ss, 8, 16);
+      ss = row_sum16(ss);
       const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + 1e-5f);
       const bool is_q = !kKOnly && rr < H;
       float oa[4], ob[4];
@@ -324,11 +349,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void qk_prologue_bwd_kernel(
         tdot = fmaf(g_a[e], x_a[e], tdot);
         tdot = fmaf(g_b[e], x_b[e], tdot);
       }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        ss += __shfl_xor(ss, m, 16);
-        tdot += __shfl_xor(tdot, m, 16);
-      }
+      ss = row_sum16(ss);
+      tdot = row_sum16(tdot);
       const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + 1e-5f);
       const float corr = r * r * r * tdot * (1.0f / kHeadDim);
       float oa[4], ob[4];
