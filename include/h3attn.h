@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 7
+#define H3ATTN_ABI_VERSION 8
 #define H3ATTN_HEAD_DIM 128
 
 /* Status codes. */
@@ -184,6 +184,41 @@ int h3attn_forward_log2(const void* q, const void* k, const void* vt, void* out,
  */
 int h3attn_kv_prologue(void* k, const void* v, const float* gamma_k, const int32_t* pos_thw, float* rope_cs,
                        void* vt, int64_t L, int32_t H, hipStream_t stream);
+
+/*
+ * Quantized-score variant (the "next" item of a quantized QK^T attention in the
+ * spirit of the SageAttention baseline the "H3 Parity Evidence Ledger" page
+ * names; MiniMax-H3 WS1/WS2 kernel roadmap RFC, section 4: a split or cast
+ * outside the contract must be declared): the scores are computed from Q' and K'
+ * rounded to OCP FP8 e4m3 (round to nearest even) on the FP8 matrix
+ * instruction, everything else as the scale-folded fused path.  Its output is
+ * NOT the bf16 path's: it follows
+ *   out = softmax_2( e4m3(4 q') e4m3(k'/4)^T ) v,   softmax_2(s)_j = 2^s_j / sum 2^s
+ * with q' = q_scale * prologue(q) and k' = prologue(k) evaluated in fp32, and
+ * carries e4m3's 3-bit mantissa in every score term (about 3-4% relative L2
+ * against the exact attention on ordinary inputs, much more where a few keys
+ * dominate).  Use it where that accuracy is declared acceptable.
+ *
+ * h3attn_kv_prologue_fp8: as h3attn_kv_prologue (rope_cs and vt the same bits),
+ *   but K's prologue output, divided by 4, goes to k8 as e4m3 bytes instead of
+ *   back to k: k8 is caller-owned, L * H * 128 bytes, 16-byte aligned, one
+ *   128-byte row per (token, head) with its channels in the order the attention
+ *   kernel reads them (byte 64 g + 32 s + 8 j + e holds channel
+ *   16 (4 s + j) + 8 g + e); k is read only.  rope_cs, k8 and vt must not overlap
+ *   one another or k, v, gamma_k, pos_thw.
+ *
+ * h3attn_forward_fp8_qprologue: attention of the raw q (Q's prologue with
+ *   gamma_q, the rope_cs table and q_scale applied at the load, then times 4 and
+ *   rounded to e4m3) against k8 and vt from h3attn_kv_prologue_fp8; q_scale =
+ *   scale * log2(e) for softmax scale `scale`.  Arguments as for
+ *   h3attn_forward_log2_qprologue, with k8 in place of k.  Precondition (device
+ *   data, not checked): |4 q'| and |k'/4| below 448, the largest e4m3 value
+ *   (prologue outputs are at most sqrt(128) max|gamma| in magnitude).
+ */
+int h3attn_kv_prologue_fp8(const void* k, const void* v, const float* gamma_k, const int32_t* pos_thw,
+                           float* rope_cs, void* k8, void* vt, int64_t L, int32_t H, hipStream_t stream);
+int h3attn_forward_fp8_qprologue(const void* q, const void* k8, const void* vt, void* out, const float* gamma_q,
+                                 const float* rope_cs, int64_t L, int32_t H, float q_scale, hipStream_t stream);
 
 int64_t h3attn_rope_table_bytes(int64_t L, int32_t H);
 int h3attn_k_prologue_table(void* k, const float* gamma_k, const int32_t* pos_thw, float* rope_cs,

@@ -23,7 +23,8 @@ EXPORTED_SYMBOLS = ("h3attn_qk_prologue", "h3attn_forward", "h3attn_qk_prologue_
                     "h3attn_qk_prologue_backward_workspace_bytes", "h3attn_qk_prologue_backward",
                     "h3attn_rope_table_bytes", "h3attn_k_prologue_table", "h3attn_forward_log2_qprologue",
                     "h3attn_forward_log2_lse", "h3attn_qk_prologue_backward_scaled",
-                    "h3attn_attention_backward_noalloc", "h3attn_kv_prologue",
+                    "h3attn_attention_backward_noalloc", "h3attn_kv_prologue", "h3attn_kv_prologue_fp8",
+                    "h3attn_forward_fp8_qprologue",
                     "h3attn_strerror", "h3attn_last_error", "h3attn_abi_version")
 
 _lock = threading.Lock()
@@ -83,6 +84,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.h3attn_attention_backward_noalloc.restype = ctypes.c_int
         lib.h3attn_kv_prologue.argtypes = [vp] * 6 + [i64, i32, vp]
         lib.h3attn_kv_prologue.restype = ctypes.c_int
+        lib.h3attn_kv_prologue_fp8.argtypes = [vp] * 7 + [i64, i32, vp]
+        lib.h3attn_kv_prologue_fp8.restype = ctypes.c_int
+        lib.h3attn_forward_fp8_qprologue.argtypes = [vp] * 6 + [i64, i32, ctypes.c_float, vp]
+        lib.h3attn_forward_fp8_qprologue.restype = ctypes.c_int
         lib.h3attn_strerror.argtypes = [ctypes.c_int]
         lib.h3attn_strerror.restype = ctypes.c_char_p
         lib.h3attn_last_error.argtypes = []
@@ -252,6 +257,58 @@ def h3attn_kv_prologue(k, v, gamma_k, pos_thw, rope_cs=None, vt=None):
                                     rope_cs.data_ptr(), vt.data_ptr(), L, H, torch.cuda.current_stream(dev).cuda_stream)
     _raise_on(lib, "h3attn_kv_prologue", st)
     return rope_cs, vt
+
+
+def h3attn_kv_prologue_fp8(k, v, gamma_k, pos_thw, rope_cs=None, k8=None, vt=None):
+    """The quantized-score path's prologue: returns (rope_cs fp32 [L, 96], k8 uint8 [L, H, 128]
+    (K's prologue output / 4 as e4m3, channels in the kernel's order), vt bf16 [H, 128, Lp]);
+    k is read only."""
+    import torch
+    L, H = _lh(k)
+    dev = k.device
+    _check_tensor("k", k, torch.bfloat16, (L, H, HEAD_DIM))
+    _check_tensor("v", v, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    _check_tensor("gamma_k", gamma_k, torch.float32, (HEAD_DIM,), dev)
+    _check_tensor("pos_thw", pos_thw, torch.int32, (L, 3), dev)
+    if rope_cs is None:
+        rope_cs = torch.empty(L, 96, dtype=torch.float32, device=dev)
+    if k8 is None:
+        k8 = torch.empty(L, H, HEAD_DIM, dtype=torch.uint8, device=dev)
+    if vt is None:
+        vt = torch.empty(H, HEAD_DIM, padded_length(L), dtype=torch.bfloat16, device=dev)
+    _check_tensor("rope_cs", rope_cs, torch.float32, (L, 96), dev)
+    _check_tensor("k8", k8, torch.uint8, (L, H, HEAD_DIM), dev)
+    _check_tensor("vt", vt, torch.bfloat16, (H, HEAD_DIM, padded_length(L)), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.h3attn_kv_prologue_fp8(k.data_ptr(), v.data_ptr(), gamma_k.data_ptr(), pos_thw.data_ptr(),
+                                        rope_cs.data_ptr(), k8.data_ptr(), vt.data_ptr(), L, H,
+                                        torch.cuda.current_stream(dev).cuda_stream)
+    _raise_on(lib, "h3attn_kv_prologue_fp8", st)
+    return rope_cs, k8, vt
+
+
+def h3attn_forward_fp8_qprologue(q, k8, vt, gamma_q, rope_cs, q_scale: float, out=None):
+    """Quantized-score attention (e4m3 Q'K^T, see include/h3attn.h) of the raw q against
+    h3attn_kv_prologue_fp8's k8 and vt; returns out."""
+    import torch
+    L, H = _lh(q)
+    dev = q.device
+    _check_tensor("q", q, torch.bfloat16, (L, H, HEAD_DIM))
+    _check_tensor("k8", k8, torch.uint8, (L, H, HEAD_DIM), dev)
+    _check_tensor("vt", vt, torch.bfloat16, (H, HEAD_DIM, padded_length(L)), dev)
+    _check_tensor("gamma_q", gamma_q, torch.float32, (HEAD_DIM,), dev)
+    _check_tensor("rope_cs", rope_cs, torch.float32, (L, 96), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, torch.bfloat16, (L, H, HEAD_DIM), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.h3attn_forward_fp8_qprologue(q.data_ptr(), k8.data_ptr(), vt.data_ptr(), out.data_ptr(),
+                                              gamma_q.data_ptr(), rope_cs.data_ptr(), L, H, float(q_scale),
+                                              torch.cuda.current_stream(dev).cuda_stream)
+    _raise_on(lib, "h3attn_forward_fp8_qprologue", st)
+    return out
 
 
 def h3attn_forward_log2_qprologue(q, k, vt, gamma_q, rope_cs, q_scale: float, out=None):

@@ -153,6 +153,18 @@ __device__ __forceinline__ DmaOffsets vt_dma_offsets(int64_t vt_row_bytes, int w
   return d;
 }
 
+// K8 tile (the FP8 variant: 64 key rows of 128 bytes, the log2 variant's row
+// permutation): one 1 KiB piece per wave; slot (row r, physical chunk p) <- key
+// perm(r), bytes 16 (p ^ vswz(r)) .. +15.
+__device__ __forceinline__ DmaOffsets k8_dma_offsets(int64_t row_bytes, int wave, int lane) {
+  DmaOffsets d;
+  const int slot = wave * 64 + lane;
+  const int r = slot >> 3;
+  const int c = (slot & 7) ^ vswz(r);
+  d.off[0] = d.off[1] = (uint32_t)(perm(r) * row_bytes + 16 * c);
+  return d;
+}
+
 // A tile's DMA: the buffer resource (tile_base: first byte of the tile;
 // valid_bytes: bytes from there to the end of the valid data) and this wave's
 // LDS destination (the tile's LDS offset plus its first piece).
@@ -190,6 +202,7 @@ __device__ __forceinline__ void cold_path() { asm volatile("" ::: "memory"); }
 // ---------------------------------------------------------------- per-wave state
 struct State {
   bf16x8_t q[8];   // Q^T operand: q[ks] = Q[row][16 ks + 8 g .. +7]
+  i32x8_t q8[2];   // FP8 variant: the same 64 values, times 4, as e4m3 (k-steps of 64)
   f32x16_t o[4];   // O^T accumulators, d-blocks of 32
   f32x16_t minit;  // log2 variant: -m in every slot, the score chain's start
   float m;         // exponent offset (raw score units; log2 variant: log2 units)
@@ -217,6 +230,16 @@ __device__ __forceinline__ Addr at_buffers(const Addr& a, uint32_t kbuf, uint32_
 // Operand of the score MFMA for 32-key block kb, k-step ks.
 __device__ __forceinline__ bf16x8_t k_operand(int kb, int ks, const lds_char* lds, const Addr& b) {
   return *(const lds_bf16x8*)(lds + kb * 8192 + (b.k ^ (32u * ks)));
+}
+
+// FP8 variant: operand of the score MFMA (k = 64) for 32-key block kb, k-step
+// ks: bytes 64 g + 32 ks .. +31 of key row 32 kb + col of the K8 tile (128-byte
+// rows, chunk c of row r at c ^ vswz(r), as a V^T tile), in two 16-byte reads;
+// the per-lane base is kaddr = buf + 128 col + 16 (4 g ^ vswz(col)).
+__device__ __forceinline__ i32x8_t k8_operand(int kb, int ks, const lds_char* lds, const Addr& b) {
+  const i32x4_t lo = __builtin_bit_cast(i32x4_t, *(const lds_bf16x8*)(lds + kb * 4096 + (b.k ^ (32u * ks))));
+  const i32x4_t hi = __builtin_bit_cast(i32x4_t, *(const lds_bf16x8*)(lds + kb * 4096 + (b.k ^ (32u * ks + 16u))));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Operand of the P*V MFMA for d-block dblk, 16-key step j: two transposing
@@ -361,6 +384,7 @@ struct Ctx {
   int64_t tile_bytes;         // 64 tokens of K or row-major V
   int64_t row_bytes;          // one token row of all heads
   int64_t vt_valid;           // V^T: bytes from a tile's first byte to its last
+  int64_t krow_bytes, ktile_bytes;  // K: one token row, 64 token rows (bf16 or FP8)
   DmaOffsets kdma, vdma;
   int n_full, n_tiles, L, wave, g;
   float c;
@@ -382,6 +406,20 @@ __device__ __forceinline__ TileDma dma_vt_tile(const Ctx& x, int t, uint32_t buf
 template <bool kVT>
 __device__ __forceinline__ TileDma dma_v(const Ctx& x, int t, uint32_t buf) {
   return kVT ? dma_vt_tile(x, t, buf) : dma_tile(x, x.vbase, t, buf);
+}
+
+// K tile t (clamped to the last tile), bf16 rows or FP8 rows.
+template <bool kFp8>
+__device__ __forceinline__ TileDma dma_k(const Ctx& x, int t, uint32_t buf) {
+  t = t < x.n_tiles ? t : x.n_tiles - 1;
+  const int64_t valid = (int64_t)(x.L - 1 - t * kBN) * x.krow_bytes + (kFp8 ? kD : kD * 2);
+  return tile_dma(x.kbase + t * x.ktile_bytes, valid, x.lds_base + buf, x.wave);
+}
+// All of this wave's pieces of a K tile (an FP8 tile has one piece a wave).
+template <bool kFp8>
+__device__ __forceinline__ void dma_k_all(const TileDma& t, const DmaOffsets& d) {
+  if (kFp8) dma_piece(t, d, 0);
+  else dma_all(t, d);
 }
 
 __device__ __forceinline__ uint32_t ring(int t) { return (uint32_t)(t % kStages) * kTileBytes; }
@@ -413,12 +451,18 @@ __device__ __forceinline__ bf16x8_t slot_operand(int k, const lds_char* lds, con
 // 4x4x4 MFMA that adds two packed pairs to the row sum.  A slot then holds one
 // transcendental and one or two plain VALU instructions next to its 32-cycle
 // matrix instruction; four more slots without one finish the last pairs.
-template <bool kPV, bool kLog2, bool kVT>
+// DMA instructions a wave issues per iteration: two pieces of each 16 KiB
+// tile, one of an FP8 K tile.
+template <bool kFp8>
+constexpr int dma_per_iteration() { return (kFp8 ? 1 : kDmaPerWave) + kDmaPerWave; }
+
+template <bool kPV, bool kLog2, bool kVT, bool kFp8>
 __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, const f32x16_t (&s_cur)[2],
                                           f32x16_t (&s_next)[2], const bf16x8_t (&p_prev)[4],
                                           bf16x8_t (&p_cur)[4], int t) {
+  static_assert(!kFp8 || (kLog2 && kVT), "the FP8 score product is built on the log2 kernel");
   asm volatile("" : "+v"(a.k), "+v"(a.v0), "+v"(a.v1));
-  const TileDma kd = dma_tile(x, x.kbase, t + kStages, ring(t));
+  const TileDma kd = dma_k<kFp8>(x, t + kStages, ring(t));
   const TileDma vd = dma_v<kVT>(x, t + kStages - 2, kVRing + ring(t + kStages - 2));
   const Addr b = at_buffers(a, ring(t + 1), kVRing + ring(t + kStages - 1));
 
@@ -426,7 +470,61 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
   float psum;
   s_next[0] = kLog2 ? st.minit : f32x16_t{};
   s_next[1] = kLog2 ? st.minit : f32x16_t{};
-  if (kPV) {
+  if (kFp8 && kPV) {
+    // Twenty matrix slots: score MFMA i (k = 64: 32-key block i & 1, k-step
+    // i >> 1; twice the issue time of the others) at slot 5 i, P*V MFMA n
+    // (d-block n & 3, 16-key step n >> 2) at slot n + n / 4 + 1.  Weights two
+    // scores a slot: slot s < 16 exponentiates scores 2s and 2s + 1, slots 1..16
+    // pack pair s - 1, and slots 3, 5, .., 17 add pairs s - 3 and s - 2 to the
+    // row sum (4x4x4 MFMA).  Operands are read two slots ahead.
+    float xs[32];
+    uint32_t w[16];
+    const i16x4_t ones4 = {16256, 16256, 16256, 16256};  // bf16 1.0
+    f32x4_t sum4 = {0.f, 0.f, 0.f, 0.f};
+    i32x8_t kop[4];
+    bf16x8_t vop[16];
+    const auto load_op = [&](int sl) {
+      if (sl % 5 == 0) {
+        kop[sl / 5] = k8_operand((sl / 5) & 1, (sl / 5) >> 1, x.lds, b);
+      } else {
+        const int n = sl - sl / 5 - 1;
+        vop[n] = v_operand<true>(n & 3, n >> 2, x.lds, b);
+      }
+    };
+    load_op(0);
+    load_op(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sl = 0; sl < 20; ++sl) {
+      if (sl == 2) dma_piece(kd, x.kdma, 0);
+      if (sl == 8) dma_piece(vd, x.vdma, 0);
+      if (sl == 14) dma_piece(vd, x.vdma, 1);
+      if (sl + 2 < 20) load_op(sl + 2);
+      if (sl % 5 == 0) {
+        const int i = sl / 5;
+        s_next[i & 1] = mfma32_fp8(kop[i], st.q8[i >> 1], s_next[i & 1]);
+      } else {
+        const int n = sl - sl / 5 - 1;
+        st.o[n & 3] = mfma32(vop[n], p_prev[n >> 2], st.o[n & 3]);
+      }
+      if (sl < 16) {
+        xs[2 * sl] = __builtin_amdgcn_exp2f(s_cur[sl >> 3][(2 * sl) & 15]);
+        xs[2 * sl + 1] = __builtin_amdgcn_exp2f(s_cur[sl >> 3][(2 * sl + 1) & 15]);
+      }
+      if (sl >= 1 && sl <= 16) {
+        w[sl - 1] = pack_bf16x2(xs[2 * sl - 2], xs[2 * sl - 1]);
+        asm volatile("" : "+v"(w[sl - 1]));
+      }
+      if (sl >= 3 && sl <= 17 && (sl & 1) == 1) {
+        const int i = (sl - 3) >> 1;
+        const i16x4_t b4 = __builtin_bit_cast(i16x4_t, u32x2_t{w[2 * i], w[2 * i + 1]});
+        sum4 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ones4, b4, sum4, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    store_pairs(w, p_cur);
+    psum = sum4[0];
+  } else if (kPV) {
     float xs[32];
     uint32_t w[16];
     const i16x4_t ones4 = {16256, 16256, 16256, 16256};  // bf16 1.0
@@ -473,12 +571,19 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     store_pairs(w, p_cur);
     psum = sum4[0];
   } else {
-    dma_all(kd, x.kdma);
+    dma_k_all<kFp8>(kd, x.kdma);
     dma_all(vd, x.vdma);
+    if (kFp8) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s_next[kb] = mfma32(k_operand(kb, ks, x.lds, b), st.q[ks], s_next[kb]);
+        for (int kb = 0; kb < 2; ++kb) s_next[kb] = mfma32_fp8(k8_operand(kb, ks, x.lds, b), st.q8[ks], s_next[kb]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s_next[kb] = mfma32(k_operand(kb, ks, x.lds, b), st.q[ks], s_next[kb]);
+    }
     psum = kLog2 ? weights(s_cur, 1.f, 0.f, p_cur) : weights(s_cur, c, mc, p_cur);
   }
   if (__builtin_amdgcn_ballot_w64(!(psum <= kSumBound)) != 0) {
@@ -490,7 +595,7 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     cold_path();
     mask_tail<kVT>(s_next, (t + 1) * kBN, x.L, x.g);
   }
-  dma_wait_all_but<(kStages - 2) * 2 * kDmaPerWave>();  // the last two iterations' DMA may be in flight
+  dma_wait_all_but<(kStages - 2) * dma_per_iteration<kFp8>()>();  // the last two iterations' DMA may be in flight
   __syncthreads();  // K(t+2), V(t) landed; every wave is done with K(t+1), V(t-1)
 }
 
@@ -498,15 +603,15 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
 // of a head) still carries its share of the tile DMA and takes part in every
 // barrier, so the other waves see the same ring; it computes nothing, which
 // leaves its SIMD's matrix core to the wave that shares it.
-template <bool kVT>
+template <bool kVT, bool kFp8>
 __device__ __forceinline__ void stream_only(const Ctx& x) {
   dma_wait();
   __syncthreads();  // the ring fill is in LDS
   __syncthreads();  // the first tile's scores are read
   for (int t = 0; t < x.n_tiles; ++t) {
-    dma_all(dma_tile(x, x.kbase, t + kStages, ring(t)), x.kdma);
+    dma_k_all<kFp8>(dma_k<kFp8>(x, t + kStages, ring(t)), x.kdma);
     dma_all(dma_v<kVT>(x, t + kStages - 2, kVRing + ring(t + kStages - 2)), x.vdma);
-    dma_wait_all_but<(kStages - 2) * 2 * kDmaPerWave>();
+    dma_wait_all_but<(kStages - 2) * dma_per_iteration<kFp8>()>();
     __syncthreads();
   }
   dma_wait();
@@ -528,8 +633,15 @@ __device__ __forceinline__ void stream_only(const Ctx& x) {
 // xor 1 (over o) and xor 4, 8 (over m) inside the lane, xor 2 the exchange
 // between the two halves.  IEEE addition commutes, so every partner order
 // gives the same sum.  cs_row: the row's cosines (48) then sines (48).
-__device__ __forceinline__ void q_prologue(bf16x8_t (&q)[8], int g, const float* __restrict__ gamma_q,
-                                           const float* __restrict__ cs_row, float q_scale) {
+//
+// kFp8: the rotated fp32 values, times 4 (exact), are rounded to FP8 e4m3
+// instead of bf16 and land in q8: channel 16 ks + 8 g + e (the value q[ks][e]
+// would hold) goes to byte 8 (ks % 4) + e of k-step ks / 4 -- the byte order of
+// a K8 row's lane half g, so the score product pairs equal channels.
+template <bool kFp8>
+__device__ __forceinline__ void q_prologue(bf16x8_t (&q)[8], i32x8_t (&q8)[2], int g,
+                                           const float* __restrict__ gamma_q, const float* __restrict__ cs_row,
+                                           float q_scale) {
   f32x4_t gm[8][2], cs[3][2], sn[3][2];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
@@ -564,23 +676,40 @@ __device__ __forceinline__ void q_prologue(bf16x8_t (&q)[8], int g, const float*
   for (int m = 0; m < 4; ++m) {
     const int ka = m < 3 ? m : 6, kb = m < 3 ? m + 3 : 7;
     bf16x8_t oa, ob;
+    float fa[8], fb[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float c = m < 3 ? cs[m][e >> 2][e & 3] : 1.0f;
       const float sv = m < 3 ? sn[m][e >> 2][e & 3] : 0.0f;
       const float ya = (float)q[ka][e] * r * (gm[ka][e >> 2][e & 3] * q_scale);
       const float yb = (float)q[kb][e] * r * (gm[kb][e >> 2][e & 3] * q_scale);
-      oa[e] = (__bf16)fmaf(ya, c, -(yb * sv));  // round to nearest even
-      ob[e] = (__bf16)fmaf(yb, c, ya * sv);
+      fa[e] = fmaf(ya, c, -(yb * sv));
+      fb[e] = fmaf(yb, c, ya * sv);
+      oa[e] = (__bf16)fa[e];  // round to nearest even
+      ob[e] = (__bf16)fb[e];
     }
-    q[ka] = oa;
-    q[kb] = ob;
+    if (kFp8) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        q8[ka >> 2][2 * (ka & 3) + h] =
+            (int)pack_e4m3x4(4.0f * fa[4 * h], 4.0f * fa[4 * h + 1], 4.0f * fa[4 * h + 2], 4.0f * fa[4 * h + 3]);
+        q8[kb >> 2][2 * (kb & 3) + h] =
+            (int)pack_e4m3x4(4.0f * fb[4 * h], 4.0f * fb[4 * h + 1], 4.0f * fb[4 * h + 2], 4.0f * fb[4 * h + 3]);
+      }
+    } else {
+      q[ka] = oa;
+      q[kb] = ob;
+    }
   }
 }
 
 // kQPro: q holds the raw (pre-prologue) rows and q_prologue is applied at
 // the load, with gamma_q, the rope_cs table ([L][96] fp32) and q_scale.
-template <bool kLog2, bool kVT, bool kQPro>
+// kFp8 (with the other three): the score product in OCP FP8 e4m3 -- q' times 4
+// quantized in the Q prologue, k' / 4 read from the K8 form h3attn_kv_prologue_fp8
+// writes (bytes [L][H][128]) -- on v_mfma_scale_f32_32x32x64_f8f6f4 at twice the
+// bf16 rate; the softmax, P V and output are those of the log2 variant.
+template <bool kLog2, bool kVT, bool kQPro, bool kFp8 = false>
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, float* __restrict__ lse, int L, int H, int Lp, float scale_log2e, int n_qfull,
@@ -622,8 +751,10 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   x.n_full = L / kBN;                              // tiles with 64 real keys
   x.n_tiles = (L + kBN - 1) / kBN;                 // plus one partial tile if L % 64 != 0
   x.tile_bytes = (int64_t)kBN * x.row_bytes;
-  x.kbase = reinterpret_cast<const char*>(k + (int64_t)head * kD);
-  x.kdma = dma_offsets<kVT>(tok_stride, x.wave, lane);
+  x.krow_bytes = kFp8 ? tok_stride : x.row_bytes;  // K8: one byte per value
+  x.ktile_bytes = (int64_t)kBN * x.krow_bytes;
+  x.kbase = reinterpret_cast<const char*>(k) + (int64_t)head * kD * (kFp8 ? 1 : 2);
+  x.kdma = kFp8 ? k8_dma_offsets(x.krow_bytes, x.wave, lane) : dma_offsets<kVT>(tok_stride, x.wave, lane);
   if (kVT) {
     const int64_t vt_row_bytes = (int64_t)Lp * 2;  // one channel row of V^T
     x.vbase = reinterpret_cast<const char*>(v + (int64_t)head * kD * Lp);
@@ -636,7 +767,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   }
 
   Addr a;
-  a.k = 256u * col + ((16u * x.g) ^ (16u * swz(col)));
+  a.k = kFp8 ? 128u * col + 16u * ((4u * x.g) ^ vswz(col)) : 256u * col + ((16u * x.g) ^ (16u * swz(col)));
   if (kVT) {
     a.v0 = 128u * col + 16u * (x.g ^ vswz(col));  // V^T row col, chunk g (XOR 2j per key step)
     a.v1 = a.v0;
@@ -649,12 +780,12 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
 
   // Ring fill: K(0) .. K(3), V(0) and V(1).
 #pragma unroll
-  for (int i = 0; i < kStages; ++i) dma_all(dma_tile(x, x.kbase, i, ring(i)), x.kdma);
+  for (int i = 0; i < kStages; ++i) dma_k_all<kFp8>(dma_k<kFp8>(x, i, ring(i)), x.kdma);
 #pragma unroll
   for (int i = 0; i < kStages - 2; ++i) dma_all(dma_v<kVT>(x, i, kVRing + ring(i)), x.vdma);
 
   if (qtile * kBM + x.wave * 32 >= L) {
-    stream_only<kVT>(x);
+    stream_only<kVT, kFp8>(x);
     return;
   }
 
@@ -665,10 +796,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     const uint16_t* p = q + (int64_t)qrow * tok_stride + (int64_t)head * kD + 8 * x.g;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) st.q[ks] = *reinterpret_cast<const bf16x8_t*>(p + 16 * ks);
-    if (kQPro) q_prologue(st.q, x.g, gamma_q, rope_cs + (int64_t)qrow * 96, q_scale);
+    if (kQPro) q_prologue<kFp8>(st.q, st.q8, x.g, gamma_q, rope_cs + (int64_t)qrow * 96, q_scale);
   } else {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) st.q[ks] = bf16x8_t{};
+    st.q8[0] = st.q8[1] = i32x8_t{};
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.o[i] = f32x16_t{};
@@ -683,10 +815,17 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   s0[1] = f32x16_t{};
   {
     const Addr b0 = at_buffers(a, ring(0), kVRing);
+    if (kFp8) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s0[kb] = mfma32(k_operand(kb, ks, x.lds, b0), st.q[ks], s0[kb]);
+        for (int kb = 0; kb < 2; ++kb) s0[kb] = mfma32_fp8(k8_operand(kb, ks, x.lds, b0), st.q8[ks], s0[kb]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s0[kb] = mfma32(k_operand(kb, ks, x.lds, b0), st.q[ks], s0[kb]);
+    }
   }
   if (x.n_full == 0) mask_tail<kVT>(s0, 0, L, x.g);
   if (kLog2) {
@@ -711,16 +850,16 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   __syncthreads();
 
   // S(t) and P(t) live in s/p[t % 2]; odd/even pairs keep that choice static.
-  iteration<false, kLog2, kVT>(x, st, a, s0, s1, p1, p0, 0);
+  iteration<false, kLog2, kVT, kFp8>(x, st, a, s0, s1, p1, p0, 0);
   int t = 1;
   for (; t + 1 < x.n_tiles; t += 2) {
-    iteration<true, kLog2, kVT>(x, st, a, s1, s0, p0, p1, t);
-    iteration<true, kLog2, kVT>(x, st, a, s0, s1, p1, p0, t + 1);
+    iteration<true, kLog2, kVT, kFp8>(x, st, a, s1, s0, p0, p1, t);
+    iteration<true, kLog2, kVT, kFp8>(x, st, a, s0, s1, p1, p0, t + 1);
   }
   // P(n-1) V(n-1); V(n-1) landed before the last iteration's barrier.
   const Addr b_last = at_buffers(a, 0, kVRing + ring(x.n_tiles - 1));
   if (t < x.n_tiles) {
-    iteration<true, kLog2, kVT>(x, st, a, s1, s0, p0, p1, t);
+    iteration<true, kLog2, kVT, kFp8>(x, st, a, s1, s0, p0, p1, t);
     pv<kVT>(st, p1, x.lds, b_last);
   } else {
     pv<kVT>(st, p0, x.lds, b_last);
@@ -773,6 +912,16 @@ hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const 
   else
     hipLaunchKernelGGL((attention_fwd_kernel<false, false, false>), grid, dim3(kThreads), 0, stream, q, k, v, out,
                        lse, (int)L, (int)H, 0, scale * kLog2e, n_qfull, nullptr, nullptr, 1.0f);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_forward_fp8(const uint16_t* q_raw, const uint8_t* k8, const uint16_t* vt, uint16_t* out,
+                                        const float* gamma_q, const float* rope_cs, int64_t L, int32_t H,
+                                        float q_scale, hipStream_t stream) {
+  const int n_qfull = (int)(L / kBM);
+  hipLaunchKernelGGL((attention_fwd_kernel<true, true, true, true>), dim3((unsigned)attention_grid_blocks(L, H)),
+                     dim3(kThreads), 0, stream, q_raw, reinterpret_cast<const uint16_t*>(k8), vt, out, nullptr,
+                     (int)L, (int)H, (int)vt_padded_length(L), 1.0f, n_qfull, gamma_q, rope_cs, q_scale);
   return hipGetLastError();
 }
 

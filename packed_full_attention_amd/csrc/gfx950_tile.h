@@ -15,6 +15,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -26,6 +27,21 @@ typedef __attribute__((address_space(3))) const f32x4_t lds_f32x4;
 // D = A B + C for a 32x32 block with k = 16 (bf16 in, fp32 out).
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D = A B + C for a 32x32 block with k = 64, A and B in OCP FP8 e4m3 (32
+// bytes a lane), fp32 out: the gfx950 block-scaled instruction with every block
+// scale at 2^0 (E8M0 127), i.e. the plain product.  Lane (g, i) holds row
+// (column) i of A (B) and a half of the 64 k values; any assignment of k
+// values to bytes works as long as A and B use the same one.
+__device__ __forceinline__ f32x16_t mfma32_fp8(i32x8_t a, i32x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+}
+
+// Four fp32 values -> four OCP FP8 e4m3 bytes, round to nearest even.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

@@ -264,6 +264,62 @@ int h3attn_kv_prologue(void* k, const void* v, const float* gamma_k, const int32
   return ok();
 }
 
+int h3attn_kv_prologue_fp8(const void* k, const void* v, const float* gamma_k, const int32_t* pos_thw,
+                           float* rope_cs, void* k8, void* vt, int64_t L, int32_t H, hipStream_t stream) {
+  if (!k || !v || !gamma_k || !pos_thw || !rope_cs || !k8 || !vt) return fail(H3A_EINVAL, "null pointer argument%s");
+  uint64_t bytes = 0;
+  if (int s = check_shape(L, H, &bytes)) return s;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(rope_cs, 16) || !aligned(vt, 16) || !aligned(k8, 16))
+    return fail(H3A_EINVAL, "k, v, rope_cs, k8 and vt must be 16-byte aligned%s");
+  if (!aligned(gamma_k, 4) || !aligned(pos_thw, 4))
+    return fail(H3A_EINVAL, "gamma_k and pos_thw must be 4-byte aligned%s");
+  // Written: rope_cs, k8, vt; read: k, v, gamma_k, pos_thw.
+  const uint64_t tbytes = (uint64_t)L * 96 * 4, vtb = (uint64_t)h3attn::vt_bytes(L, H), pbytes = (uint64_t)L * 12;
+  const void* wr[3] = {rope_cs, k8, vt};
+  const uint64_t wn[3] = {tbytes, bytes / 2, vtb};
+  const void* in[4] = {k, v, gamma_k, pos_thw};
+  const uint64_t inn[4] = {bytes, bytes, 512, pbytes};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlap(wr[i], wn[i], in[j], inn[j]))
+        return fail(H3A_EINVAL, "rope_cs, k8 or vt overlaps k, v, gamma_k or pos_thw%s");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(wr[i], wn[i], wr[j], wn[j])) return fail(H3A_EINVAL, "rope_cs, k8 and vt overlap%s");
+  }
+  if (h3attn::kv_prologue_grid_blocks(L, H) * h3attn::transpose_block_threads() >= kMaxThreadsPerGrid)
+    return fail(H3A_EUNSUPPORTED, "prologue grid too large for (L, H)%s");
+  if (int s = check_prologue_rows(H)) return s;
+  const hipError_t e = h3attn::launch_kv_prologue_fp8(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                                      static_cast<uint16_t*>(vt), gamma_k, pos_thw, rope_cs,
+                                                      static_cast<uint8_t*>(k8), L, H, stream);
+  if (e != hipSuccess) return fail(H3A_EHIP, "prologue launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int h3attn_forward_fp8_qprologue(const void* q, const void* k8, const void* vt, void* out, const float* gamma_q,
+                                 const float* rope_cs, int64_t L, int32_t H, float q_scale, hipStream_t stream) {
+  if (!q || !k8 || !vt || !out || !gamma_q || !rope_cs) return fail(H3A_EINVAL, "null pointer argument%s");
+  uint64_t bytes = 0;
+  if (int s = check_shape(L, H, &bytes)) return s;
+  if (!aligned(q, 16) || !aligned(k8, 16) || !aligned(vt, 16) || !aligned(out, 16) || !aligned(gamma_q, 16) ||
+      !aligned(rope_cs, 16))
+    return fail(H3A_EINVAL, "q, k8, vt, out, gamma_q and rope_cs must be 16-byte aligned%s");
+  if (!(isfinite(q_scale) && q_scale > 0.0f)) return fail(H3A_EINVAL, "q_scale must be finite and > 0%s");
+  const uint64_t vbytes = (uint64_t)h3attn::vt_bytes(L, H), tbytes = (uint64_t)L * 96 * 4;
+  if (overlap(out, bytes, q, bytes) || overlap(out, bytes, k8, bytes / 2) || overlap(out, bytes, vt, vbytes) ||
+      overlap(out, bytes, gamma_q, 512) || overlap(out, bytes, rope_cs, tbytes))
+    return fail(H3A_EINVAL, "out overlaps q, k8, vt, gamma_q or rope_cs%s");
+  if (h3attn::attention_grid_blocks(L, H) * h3attn::attention_block_threads() >= kMaxThreadsPerGrid)
+    return fail(H3A_EUNSUPPORTED, "attention grid too large for (L, H)%s");
+  if (int s = check_row_tiles(H)) return s;
+  if (int s = check_vt_tiles(L)) return s;
+  const hipError_t e = h3attn::launch_attention_forward_fp8(
+      static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k8), static_cast<const uint16_t*>(vt),
+      static_cast<uint16_t*>(out), gamma_q, rope_cs, L, H, q_scale, stream);
+  if (e != hipSuccess) return fail(H3A_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int h3attn_forward_log2_qprologue(const void* q, const void* k, const void* vt, void* out, const float* gamma_q,
                                   const float* rope_cs, int64_t L, int32_t H, float q_scale, hipStream_t stream) {
   if (!q || !k || !vt || !out || !gamma_q || !rope_cs) return fail(H3A_EINVAL, "null pointer argument%s");

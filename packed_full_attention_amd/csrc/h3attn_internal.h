@@ -36,6 +36,13 @@ hipError_t launch_attention_forward_qprologue(const uint16_t* q_raw, const uint1
                                               uint16_t* out, const float* gamma_q, const float* rope_cs,
                                               int64_t L, int32_t H, float q_scale, hipStream_t stream);
 
+// The quantized-score variant: Q's prologue at the load as above, its output
+// times 4 rounded to FP8 e4m3, scores against k8 (h3attn_kv_prologue_fp8's FP8
+// K, k'/4) on the FP8 matrix instruction; softmax and P V as the log2 variant.
+hipError_t launch_attention_forward_fp8(const uint16_t* q_raw, const uint8_t* k8, const uint16_t* vt, uint16_t* out,
+                                        const float* gamma_q, const float* rope_cs, int64_t L, int32_t H,
+                                        float q_scale, hipStream_t stream);
+
 // Enqueue the attention backward (two kernels, in this order): dq and the
 // per-row statistics -lse log2(e) and -delta = -<dout, out> (stats, fp32
 // [2][H][Lp], Lp = L rounded up to 64; written), then dk and dv.  q, k are
@@ -74,6 +81,13 @@ hipError_t launch_v_transpose(const uint16_t* v, uint16_t* vt, int64_t L, int32_
 hipError_t launch_kv_prologue(uint16_t* k, const uint16_t* v, uint16_t* vt, const float* gamma_k, const int32_t* pos,
                               float* rope_cs, int64_t L, int32_t H, hipStream_t stream);
 int64_t kv_prologue_grid_blocks(int64_t L, int32_t H);
+
+// launch_kv_prologue with K's prologue output written as FP8 e4m3 to k8
+// (bytes [L][H][128], each value k'/4, channels ordered as the FP8 attention
+// kernel reads them) instead of back to k (read only).
+hipError_t launch_kv_prologue_fp8(const uint16_t* k, const uint16_t* v, uint16_t* vt, const float* gamma_k,
+                                  const int32_t* pos, float* rope_cs, uint8_t* k8, int64_t L, int32_t H,
+                                  hipStream_t stream);
 int64_t vt_padded_length(int64_t L);
 int64_t vt_bytes(int64_t L, int32_t H);
 int64_t transpose_grid_blocks(int64_t L, int32_t H);

@@ -78,15 +78,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// FP8 form of K (the quantized-score path): byte position of channel c in a
+// 128-byte k8 row.  The row is laid out as the attention kernel's FP8 score
+// product reads it -- lane half g's 64 bytes first for g = 0, then g = 1, each
+// two 32-byte k-steps of four 8-channel pieces -- so that a lane's operand is
+// one contiguous read:  position 64 g + 32 s + 8 j + e holds channel
+// 16 (4 s + j) + 8 g + e.
+__device__ __forceinline__ int k8_position(int c) {
+  return 64 * ((c >> 3) & 1) + 32 * (c >> 6) + 8 * ((c >> 4) & 3) + (c & 7);
+}
+
+// Four fp32 values -> four OCP FP8 e4m3 bytes (round to nearest even; the
+// values here stay far inside the format's range).
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
 // One wave's work: every head row of one token (Q's, then K's).  kKOnly:
 // only K's rows, and the lane's cosines and sines go to rope_cs (fp32 [L][96]:
 // cos of the token's 48 angles, then their sines) for an attention kernel that
-// applies Q's prologue itself.
-template <int kPassesPerChunk, bool kKOnly>
+// applies Q's prologue itself.  kK8 (with kKOnly): K's outputs, times 1/4, go to
+// k8 as FP8 e4m3 (bytes ordered by k8_position) instead of back to k as bf16.
+template <int kPassesPerChunk, bool kKOnly, bool kK8 = false>
 __device__ __forceinline__ void prologue_token(uint16_t* __restrict__ q, uint16_t* __restrict__ k,
                                                const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
                                                const int32_t* __restrict__ pos, int64_t token, int32_t H,
-                                               float q_scale, float* __restrict__ rope_cs, int lane) {
+                                               float q_scale, float* __restrict__ rope_cs, int lane,
+                                               uint8_t* __restrict__ k8 = nullptr) {
+  static_assert(!kK8 || kKOnly, "the FP8 form is written for K alone");
   const int sub = lane >> 4;  // which of the pass's 4 rows this quarter-wave owns
   const int i = lane & 15;    // lane within the row
   const bool pair_lane = i < 12;
@@ -157,7 +177,13 @@ __device__ __forceinline__ void prologue_token(uint16_t* __restrict__ q, uint16_
         oa[e] = fmaf(ya, cs[e], -(yb * sn[e]));
         ob[e] = fmaf(yb, cs[e], ya * sn[e]);
       }
-      if (rr < rows) {
+      if (kK8 && rr < rows) {
+        uint8_t* row8 = k8 + token_base + (int64_t)rr * kHeadDim;
+        *reinterpret_cast<uint32_t*>(row8 + k8_position(ch_a)) =
+            pack_e4m3x4(0.25f * oa[0], 0.25f * oa[1], 0.25f * oa[2], 0.25f * oa[3]);
+        *reinterpret_cast<uint32_t*>(row8 + k8_position(ch_b)) =
+            pack_e4m3x4(0.25f * ob[0], 0.25f * ob[1], 0.25f * ob[2], 0.25f * ob[3]);
+      } else if (rr < rows) {
         uint16_t* row = (is_q ? q : k) + token_base + (int64_t)(kKOnly || is_q ? rr : rr - H) * kHeadDim;
         *reinterpret_cast<uint2*>(row + ch_a) = make_uint2(pack_bf16x2(oa[0], oa[1]), pack_bf16x2(oa[2], oa[3]));
         *reinterpret_cast<uint2*>(row + ch_b) = make_uint2(pack_bf16x2(ob[0], ob[1]), pack_bf16x2(ob[2], ob[3]));
@@ -237,19 +263,19 @@ __global__ __launch_bounds__(kVtThreads) void v_transpose_kernel(const uint16_t*
 // whole launch instead of running one after the other.
 static_assert(kWavesPerBlock * 64 == kVtThreads, "both kinds of workgroup have 256 threads");
 
-template <int kPassesPerChunk>
+template <int kPassesPerChunk, bool kK8>
 __global__ __launch_bounds__(kVtThreads) void kv_prologue_kernel(
     uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ vt,
     const float* __restrict__ gamma_k, const int32_t* __restrict__ pos, float* __restrict__ rope_cs, int64_t L,
-    int32_t H, int Lp, int64_t nk, int64_t n) {
+    int32_t H, int Lp, int64_t nk, int64_t n, uint8_t* __restrict__ k8) {
   __shared__ uint32_t tile[kVtTileWords];
   const int64_t b = blockIdx.x;
   const int64_t kb = b * nk / n;
   if ((b + 1) * nk / n > kb) {
     const int64_t token = kb * kWavesPerBlock + (threadIdx.x >> 6);
     if (token < L)
-      prologue_token<kPassesPerChunk, true>(nullptr, k, gamma_k, gamma_k, pos, token, H, 1.0f, rope_cs,
-                                            threadIdx.x & 63);
+      prologue_token<kPassesPerChunk, true, kK8>(nullptr, k, gamma_k, gamma_k, pos, token, H, 1.0f, rope_cs,
+                                                 threadIdx.x & 63, k8);
     return;
   }
   const int64_t vb = b - kb;  // V workgroups before this one
@@ -502,26 +528,38 @@ hipError_t launch_k_prologue(uint16_t* k, const float* gamma_k, const int32_t* p
   return hipGetLastError();
 }
 
-hipError_t launch_kv_prologue(uint16_t* k, const uint16_t* v, uint16_t* vt, const float* gamma_k, const int32_t* pos,
-                              float* rope_cs, int64_t L, int32_t H, hipStream_t stream) {
+template <bool kK8>
+static hipError_t launch_kv(uint16_t* k, const uint16_t* v, uint16_t* vt, const float* gamma_k, const int32_t* pos,
+                            float* rope_cs, uint8_t* k8, int64_t L, int32_t H, hipStream_t stream) {
   const int64_t nk = prologue_grid_blocks(L), n = kv_prologue_grid_blocks(L, H);
   const int Lp = (int)vt_padded_length(L);
   const dim3 grid((unsigned)n), block(kVtThreads);
   switch (prologue_passes(H)) {
     case 14:
-      hipLaunchKernelGGL(kv_prologue_kernel<14>, grid, block, 0, stream, k, v, vt, gamma_k, pos, rope_cs, L, H, Lp,
-                         nk, n);
+      hipLaunchKernelGGL((kv_prologue_kernel<14, kK8>), grid, block, 0, stream, k, v, vt, gamma_k, pos, rope_cs, L,
+                         H, Lp, nk, n, k8);
       break;
     case 8:
-      hipLaunchKernelGGL(kv_prologue_kernel<8>, grid, block, 0, stream, k, v, vt, gamma_k, pos, rope_cs, L, H, Lp,
-                         nk, n);
+      hipLaunchKernelGGL((kv_prologue_kernel<8, kK8>), grid, block, 0, stream, k, v, vt, gamma_k, pos, rope_cs, L,
+                         H, Lp, nk, n, k8);
       break;
     default:
-      hipLaunchKernelGGL(kv_prologue_kernel<4>, grid, block, 0, stream, k, v, vt, gamma_k, pos, rope_cs, L, H, Lp,
-                         nk, n);
+      hipLaunchKernelGGL((kv_prologue_kernel<4, kK8>), grid, block, 0, stream, k, v, vt, gamma_k, pos, rope_cs, L,
+                         H, Lp, nk, n, k8);
       break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_kv_prologue(uint16_t* k, const uint16_t* v, uint16_t* vt, const float* gamma_k, const int32_t* pos,
+                              float* rope_cs, int64_t L, int32_t H, hipStream_t stream) {
+  return launch_kv<false>(k, v, vt, gamma_k, pos, rope_cs, nullptr, L, H, stream);
+}
+
+hipError_t launch_kv_prologue_fp8(const uint16_t* k, const uint16_t* v, uint16_t* vt, const float* gamma_k,
+                                  const int32_t* pos, float* rope_cs, uint8_t* k8, int64_t L, int32_t H,
+                                  hipStream_t stream) {
+  return launch_kv<true>(const_cast<uint16_t*>(k), v, vt, gamma_k, pos, rope_cs, k8, L, H, stream);
 }
 
 // Workspace of the backward: one 256-float partial per workgroup, then one per

@@ -71,3 +71,36 @@ def attention_backward_heads(q, k, v, do, scale: float, heads):
     heads = [int(h) for h in heads]
     res = _run(lambda h: ob.attention_head_backward(q[:, h], k[:, h], v[:, h], do[:, h], scale), heads)
     return dict(zip(heads, res))
+
+
+def packed_attention_fp8_full(q_bits, k_bits, v_bits, gamma_q, gamma_k, pos, q_scale: float, heads=None,
+                              exact_scale=None, block: int = 512):
+    """The quantized-score path (oracle.rms_norm -> oracle.mm_rope ->
+    oracle.quantized_operands -> oracle.quantized_attention_head) for the listed
+    heads (all by default) of bf16 [L, H, 128] q, k, v.  Returns float64
+    (out_fp8, k', out_exact): [L, n_heads, 128] each; out_exact (the exact path's
+    oracle.attention_head at `exact_scale`) is None unless exact_scale is given."""
+    L, H, D = q_bits.shape
+    heads = list(range(H)) if heads is None else [int(h) for h in heads]
+    n = len(heads)
+    qr, kr, q8, k8, vh = [None] * n, [None] * n, [None] * n, [None] * n, [None] * n
+
+    def prologue(i):
+        h = heads[i]
+        qr[i] = oracle.mm_rope(oracle.rms_norm(_head(q_bits, h), gamma_q), pos)
+        kr[i] = oracle.mm_rope(oracle.rms_norm(_head(k_bits, h), gamma_k), pos)
+        q8[i], k8[i] = oracle.quantized_operands(qr[i], kr[i], q_scale)
+        vh[i] = _head(v_bits, h)
+
+    _run(prologue, range(n))
+    out = np.empty((L, n, D), dtype=np.float64)
+    exact = None if exact_scale is None else np.empty((L, n, D), dtype=np.float64)
+
+    def attend(task):
+        i, r0 = task
+        out[r0:r0 + block, i] = oracle.quantized_attention_head(q8[i][r0:r0 + block], k8[i], vh[i])
+        if exact is not None:
+            exact[r0:r0 + block, i] = oracle.attention_head(qr[i][r0:r0 + block], kr[i], vh[i], exact_scale)
+
+    _run(attend, [(i, r0) for i in range(n) for r0 in range(0, L, block)])
+    return out, np.stack(kr, axis=1), exact

@@ -34,7 +34,7 @@ def test_header_declares_the_expected_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.h3attn_abi_version() == 7
+    assert lib.h3attn_abi_version() == 8
 
 
 def test_strerror_strings(lib):
@@ -139,6 +139,42 @@ def test_fused_entry_points_reject(lib):
     for out in (A, B + 256, C + 1024, G - 256, P + 4096):
         assert fq(out=out) == 1 and "overlap" in lib.h3attn_last_error().decode()
     assert fq(L=1 << 31) == 2
+
+
+def test_fp8_entry_points_reject(lib):
+    kv = lambda **kw: lib.h3attn_kv_prologue_fp8(kw.get("k", A), kw.get("v", B), kw.get("gk", G), kw.get("pos", P),
+                                                 kw.get("cs", C), kw.get("k8", O), kw.get("vt", O + (1 << 30)),
+                                                 kw.get("L", 160), kw.get("H", 4), None)
+    for kw in (dict(k=None), dict(v=None), dict(gk=None), dict(pos=None), dict(cs=None), dict(k8=None),
+               dict(vt=None)):
+        assert kv(**kw) == 1 and "null" in lib.h3attn_last_error().decode()
+    assert kv(L=0) == 1 and kv(H=0) == 1 and kv(L=-5) == 1
+    assert kv(k8=O + 8) == 1 and "aligned" in lib.h3attn_last_error().decode()
+    assert kv(gk=G + 2) == 1 and "aligned" in lib.h3attn_last_error().decode()
+    # k8 is L * H * 128 bytes; it may not overlap k (read) or vt (written)
+    for k8 in (A + 1024, B, C + 64, P - 256):
+        assert kv(k8=k8) == 1 and "overlap" in lib.h3attn_last_error().decode()
+    assert kv(vt=O + 160 * 4 * 128 - 256) == 1 and "overlap" in lib.h3attn_last_error().decode()
+    ff = lambda **kw: lib.h3attn_forward_fp8_qprologue(kw.get("q", A), kw.get("k8", B), kw.get("vt", C),
+                                                       kw.get("out", O), kw.get("gq", G), kw.get("cs", P),
+                                                       kw.get("L", 160), kw.get("H", 4), kw.get("s", 0.1275), None)
+    for kw in (dict(q=None), dict(k8=None), dict(vt=None), dict(out=None), dict(gq=None), dict(cs=None)):
+        assert ff(**kw) == 1 and "null" in lib.h3attn_last_error().decode()
+    assert ff(k8=B + 8) == 1 and "aligned" in lib.h3attn_last_error().decode()
+    for s_ in (0.0, -1.0, float("nan"), float("inf")):
+        assert ff(s=s_) == 1 and "q_scale" in lib.h3attn_last_error().decode()
+    for out in (A, B + 128, C + 1024, G - 256, P + 4096):
+        assert ff(out=out) == 1 and "overlap" in lib.h3attn_last_error().decode()
+    assert ff(L=1 << 31) == 2
+    big = FAR
+    assert lib.h3attn_forward_fp8_qprologue(big[0], big[1], big[2], big[3], big[4], big[5], 64, H_WRAP, 0.1275,
+                                            None) == 2
+    assert "2^32" in lib.h3attn_last_error().decode()
+    assert lib.h3attn_forward_fp8_qprologue(big[0], big[1], big[2], big[3], big[4], big[5], L_VT_WRAP, 1, 0.1275,
+                                            None) == 2
+    assert "vt" in lib.h3attn_last_error().decode()
+    assert lib.h3attn_kv_prologue_fp8(big[0], big[1], big[2], big[3], big[4], big[5], big[6], 1, (1 << 30) - 31,
+                                      None) == 2
 
 
 def test_training_entry_points_reject(lib):
