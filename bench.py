@@ -10,7 +10,10 @@ MM-RoPE and the factor scale * log2(e) applied at the kernel's Q load).  Its
 output is bit-identical to the unfused h3attn_qk_prologue_scaled +
 h3attn_v_transpose + h3attn_forward_log2 ("scale_folded_path") and carries the
 same roundings as h3attn_qk_prologue + h3attn_forward ("plain_path"); both are
-timed beside it.
+timed beside it, and so is the quantized-score variant ("fp8_scores_path":
+h3attn_kv_prologue_fp8 + h3attn_forward_fp8_qprologue, e4m3 Q'K^T), whose
+output follows its own declared definition and accuracy profile and so never
+enters `value`.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
                     [--no-cpu-baseline] [--copy-probe]
@@ -47,6 +50,10 @@ METRIC = "packed-attention TFLOP/s + % bf16 MFMA peak at L~16.5k, H=56; prologue
 # MI355X (gfx950) published peaks: 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU; HBM3E 8 TB/s.
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2  # dense fp8: twice the bf16 rate
+# The quantized-score kernel runs half its products (Q'K^T) at the fp8 rate and
+# half (P V) at the bf16 rate: its matrix-core ceiling is the harmonic blend.
+PEAK_FP8_BF16_MIXED_TFLOPS = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
 MAX_STEPS = 256  # warm-up + timed steps, each with its own q/k copy (473 MiB at L=16500, H=56)
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -64,6 +71,12 @@ def kv_prologue_bytes(L: int, H: int) -> float:
     # K read + written, V read, V^T written (2 B each per element), the 384 B/token
     # rotation table written, 12 B/token positions, gamma_k
     return 8.0 * L * H * 128 + 384.0 * L + 12.0 * L + 512.0
+
+
+def kv_prologue_fp8_bytes(L: int, H: int) -> float:
+    # K read (2 B), its e4m3 form written (1 B), V read and V^T written (2 B each)
+    # per element, the rotation table, positions and gamma_k as in the bf16 form
+    return 7.0 * L * H * 128 + 384.0 * L + 12.0 * L + 512.0
 
 
 def kernel_source_sha() -> str:
@@ -150,9 +163,9 @@ def main() -> int:
 
     import numpy as np
     import torch
-    from packed_full_attention_amd import (h3attn_attention_backward, h3attn_forward, h3attn_forward_log2,
-                                           h3attn_forward_log2_lse, h3attn_forward_log2_qprologue,
-                                           h3attn_kv_prologue, h3attn_qk_prologue, h3attn_qk_prologue_backward_scaled,
+    from packed_full_attention_amd import (h3attn_attention_backward, h3attn_forward, h3attn_forward_fp8_qprologue,
+                                           h3attn_forward_log2, h3attn_forward_log2_lse, h3attn_forward_log2_qprologue,
+                                           h3attn_kv_prologue, h3attn_kv_prologue_fp8, h3attn_qk_prologue, h3attn_qk_prologue_backward_scaled,
                                            h3attn_qk_prologue_scaled, h3attn_v_transpose, load_library)
     from packed_full_attention_amd import workloads as wl
 
@@ -242,6 +255,18 @@ def main() -> int:
     ms_step, (t_kv, t_att), wall_ms = timed(fused, K, W)
     del qs, ks
 
+    # The quantized-score variant reads q and k without writing them: no copies.
+    k8 = torch.empty(L, H, 128, dtype=torch.uint8, device=dev)
+    out8 = torch.empty_like(q)
+    fp8 = [lambda i: h3attn_kv_prologue_fp8(k, v, gk, pos, rope_cs, k8, vt),
+           lambda i: h3attn_forward_fp8_qprologue(q, k8, vt, gq, rope_cs, q_scale, out8)]
+    for i in range(W):
+        for f in fp8:
+            f(i)
+    fp8_ms, (t_kv8, t_att8), _ = timed(fp8, K, W)
+    fp8_finite = bool(torch.isfinite(out8.float()).all())
+    del k8, out8
+
     # Training pieces, timed separately (not part of `value`), in the scale-folded
     # layout: the log2 forward with log-sum-exp, the attention backward on
     # q' = c q at scale ln 2, and the scaled prologue backward, on the scaled
@@ -266,7 +291,7 @@ def main() -> int:
     bwd_flops = 2.5 * attention_flops(L, H)  # dV, dP, dQ, dK and the recomputed S: 5 products of 2 L^2 128
     pbwd_bytes = 12.0 * L * H * 128 + 12.0 * L + 1024.0  # read q, k, dq', dk'; write dq, dk
     del qp, kp, dout, out2, lse, dq, dk, dv, ws, pws
-    if not bool(torch.isfinite(out.float()).all()):
+    if not (bool(torch.isfinite(out.float()).all()) and fp8_finite):
         print("bench.py: non-finite attention output", file=sys.stderr)
         return 1
 
@@ -330,6 +355,16 @@ def main() -> int:
                        "attention_ms": round(plain_att, 4),
                        "attention_tflops": round(flops / (plain_att * 1e-3) / 1e12, 2),
                        "prologue_us": round(plain_pro * 1e3, 2)},
+        "fp8_scores_path": {"entry_points": "h3attn_kv_prologue_fp8 + h3attn_forward_fp8_qprologue",
+                            "numerics": "e4m3(4 q') e4m3(k'/4)^T scores, bf16 P V; its own accuracy profile "
+                                        "(about 4% relative L2 against the exact attention), not the bf16 path's",
+                            "ms_per_step": round(fp8_ms, 4), "attention_ms": round(t_att8, 4),
+                            "attention_tflops": round(flops / (t_att8 * 1e-3) / 1e12, 2),
+                            "mixed_peak_tflops": round(PEAK_FP8_BF16_MIXED_TFLOPS, 1),
+                            "frac_of_mixed_peak": round(flops / (t_att8 * 1e-3) / 1e12 / PEAK_FP8_BF16_MIXED_TFLOPS,
+                                                        4),
+                            "kv_prologue_us": round(t_kv8 * 1e3, 2),
+                            "kv_prologue_gbs": round(kv_prologue_fp8_bytes(L, H) / (t_kv8 * 1e-3) / 1e9, 1)},
         "backward": {"entry_points": "h3attn_forward_log2_lse + h3attn_attention_backward (q' = c q, scale ln 2) + "
                                      "h3attn_qk_prologue_backward_scaled",
                      "forward_lse_ms": round(t_fl, 4),
