@@ -459,25 +459,32 @@ __device__ __forceinline__ bf16x8_t fused_operand(int k, const lds_char* nxt, in
 // of this block's weights: 2e the exponent of score e, 2e+1 its exponential,
 // 2e+2 dS = P dP', and each bf16 pair packed the slot after its second value;
 // dma(k) issues the step's share of the ring DMA.
-template <bool kPrev, typename Dma>
+//
+// kUnit (c == 1, the scale-folded layout's scale ln 2): the S chain of the
+// next block starts from its rows' -lse log2(e) instead of 0, as the dP' chain
+// starts from -delta, so a score leaves the matrix core as its exponent and
+// the weight is one exponential with no FMA in front of it.
+template <bool kPrev, bool kUnit, typename Dma>
 __device__ __forceinline__ void fused_step(const lds_char* cur, int qb, const lds_char* nxt, int qbn,
                                            const lds_char* prv, int qbp, const Addr& a, float c, int g,
                                            const f32x16_t& s_c, const f32x16_t& dp_c, f32x16_t& s_n,
                                            f32x16_t& dp_n, const bf16x8_t (&wp_p)[2], const bf16x8_t (&ws_p)[2],
                                            bf16x8_t (&wp_c)[2], bf16x8_t (&ws_c)[2], FusedOps& fo, const Dma& dma) {
   float nl[16];
-  f32x16_t dinit;
+  f32x16_t dinit, ninit;
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    const f32x4_t l4 = *(const lds_f32x4*)(cur + 2 * kTileBytes + 4 * (32 * qb + 8 * rr + 4 * g));
+    const f32x4_t l4 = kUnit ? *(const lds_f32x4*)(nxt + 2 * kTileBytes + 4 * (32 * qbn + 8 * rr + 4 * g))
+                             : *(const lds_f32x4*)(cur + 2 * kTileBytes + 4 * (32 * qb + 8 * rr + 4 * g));
     const f32x4_t d4 = *(const lds_f32x4*)(nxt + 2 * kTileBytes + 1024 + 4 * (32 * qbn + 8 * rr + 4 * g));
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       nl[4 * rr + qq] = l4[qq];
+      ninit[4 * rr + qq] = l4[qq];
       dinit[4 * rr + qq] = d4[qq];
     }
   }
-  s_n = f32x16_t{};
+  s_n = kUnit ? ninit : f32x16_t{};
   dp_n = dinit;
   bf16x8_t op[32];
 #pragma unroll
@@ -502,8 +509,8 @@ __device__ __forceinline__ void fused_step(const lds_char* cur, int qb, const ld
         else fo.dka[dblk] = mfma32(op[k], ws_p[jj], fo.dka[dblk]);
       }
     }
-    if (k < 32 && (k & 1) == 0) xa[k >> 1] = fmaf(s_c[k >> 1], c, nl[k >> 1]);
-    if (k < 32 && (k & 1) == 1) p[k >> 1] = __builtin_amdgcn_exp2f(xa[k >> 1]);
+    if (!kUnit && k < 32 && (k & 1) == 0) xa[k >> 1] = fmaf(s_c[k >> 1], c, nl[k >> 1]);
+    if (k < 32 && (k & 1) == 1) p[k >> 1] = __builtin_amdgcn_exp2f(kUnit ? s_c[k >> 1] : xa[k >> 1]);
     if (k >= 2 && k <= 32 && (k & 1) == 0) x[(k - 2) >> 1] = p[(k - 2) >> 1] * dp_c[(k - 2) >> 1];
     if (k >= 4 && k <= 32 && (k & 3) == 0) {
       const int m = (k - 4) >> 2;
@@ -522,6 +529,7 @@ __device__ __forceinline__ void fused_step(const lds_char* cur, int qb, const ld
   }
 }
 
+template <bool kUnit>
 __global__ __launch_bounds__(64 * kFusedWaves, 1) void attention_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ stats, uint16_t* __restrict__ dk_out,
@@ -574,8 +582,12 @@ __global__ __launch_bounds__(64 * kFusedWaves, 1) void attention_bwd_dkdv_kernel
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const f32x4_t d4 = *(const lds_f32x4*)(lds + 2 * kTileBytes + 1024 + 4 * (8 * rr + 4 * g));
+    const f32x4_t l4 = *(const lds_f32x4*)(lds + 2 * kTileBytes + 4 * (8 * rr + 4 * g));
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) da[4 * rr + qq] = d4[qq];
+    for (int qq = 0; qq < 4; ++qq) {
+      da[4 * rr + qq] = d4[qq];
+      if (kUnit) sa[4 * rr + qq] = l4[qq];
+    }
   }
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -595,20 +607,20 @@ __global__ __launch_bounds__(64 * kFusedWaves, 1) void attention_bwd_dkdv_kernel
       if ((kslot & 3) == 1 && kslot < 32) piece(2, kslot >> 2);
       if (kslot == 3) piece(2, 8);
     };
-    fused_step<false>(slot(0), 0, slot(0), 1, slot(0), 0, a, c, g, sa, da, sb, db, wpb, wsb, wpa, wsa, fo, dma);
+    fused_step<false, kUnit>(slot(0), 0, slot(0), 1, slot(0), 0, a, c, g, sa, da, sb, db, wpb, wsb, wpa, wsa, fo, dma);
     wait_and_sync();
   }
   // The last trip's second step, block (n_tiles, 0), finishes dV and dK of the
   // last block; its own scores come from a stale (loaded) slot and are never
   // used, like those of the next block in the first step of that trip.
   for (int t = 0; t < n_tiles; ++t) {
-    fused_step<true>(slot(t), 1, slot(t + 1), 0, slot(t), 0, a, c, g, sb, db, sa, da, wpa, wsa, wpb, wsb, fo,
+    fused_step<true, kUnit>(slot(t), 1, slot(t + 1), 0, slot(t), 0, a, c, g, sb, db, sa, da, wpa, wsa, wpb, wsb, fo,
                      no_dma);
     const auto dma = [&](int kslot) {
       if ((kslot & 3) == 1 && kslot < 32) piece(t + 3, kslot >> 2);
       if (kslot == 3) piece(t + 3, 8);
     };
-    fused_step<true>(slot(t + 1), 0, slot(t + 1), 1, slot(t), 1, a, c, g, sa, da, sb, db, wpb, wsb, wpa, wsa, fo,
+    fused_step<true, kUnit>(slot(t + 1), 0, slot(t + 1), 1, slot(t), 1, a, c, g, sa, da, sb, db, wpb, wsb, wpa, wsa, fo,
                      dma);
     wait_and_sync();
   }
@@ -674,8 +686,12 @@ hipError_t launch_attention_backward(const uint16_t* q, const uint16_t* k, const
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 fgrid((unsigned)(((L + kFusedRows - 1) / kFusedRows) * (int64_t)H));
-  hipLaunchKernelGGL(attention_bwd_dkdv_kernel, fgrid, dim3(64 * kFusedWaves), 0, stream, q, k, v, dout, stats,
-                     dk, dv, (int)L, (int)H, Lp, c, scale, (int)(L / kFusedRows));
+  if (c == 1.0f)
+    hipLaunchKernelGGL(attention_bwd_dkdv_kernel<true>, fgrid, dim3(64 * kFusedWaves), 0, stream, q, k, v, dout,
+                       stats, dk, dv, (int)L, (int)H, Lp, c, scale, (int)(L / kFusedRows));
+  else
+    hipLaunchKernelGGL(attention_bwd_dkdv_kernel<false>, fgrid, dim3(64 * kFusedWaves), 0, stream, q, k, v, dout,
+                       stats, dk, dv, (int)L, (int)H, Lp, c, scale, (int)(L / kFusedRows));
   return hipGetLastError();
 }
 

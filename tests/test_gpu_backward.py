@@ -78,26 +78,26 @@ def test_forward_lse(inputs, idx):
 
 # ------------------------------------------------------------------ attention backward
 
-def _attention_case(q, k, v, seed):
+def _attention_case(q, k, v, seed, scale=SCALE):
     """GPU forward (with lse) and backward on device q, k, v; returns the
     device gradients and the bf16 dO bits."""
     L, H, _ = q.shape
     do_bits = _bf16_normal((L, H, 128), seed)
     do = dev_bf16(do_bits)
-    out, lse = h3attn_forward_lse(q, k, v, scale=SCALE)
-    dq, dk, dv = h3attn_attention_backward(q, k, v, out, do, lse, scale=SCALE)
+    out, lse = h3attn_forward_lse(q, k, v, scale=scale)
+    dq, dk, dv = h3attn_attention_backward(q, k, v, out, do, lse, scale=scale)
     torch.cuda.synchronize()
     return dq, dk, dv, do_bits
 
 
-def _compare_attention(tag, q, k, v, grads, do_bits, heads=None):
+def _compare_attention(tag, q, k, v, grads, do_bits, heads=None, scale=SCALE):
     dq, dk, dv = grads
     qf, kf, vf = host_f64(q), host_f64(k), host_f64(v)
     dof = _as_f64(do_bits)
     gq, gk, gv = host_f64(dq), host_f64(dk), host_f64(dv)
     hs = range(q.shape[1]) if heads is None else heads
     for h in hs:
-        rq, rk, rv = oracle.attention_head_backward(qf[:, h], kf[:, h], vf[:, h], dof[:, h], SCALE)
+        rq, rk, rv = oracle.attention_head_backward(qf[:, h], kf[:, h], vf[:, h], dof[:, h], scale)
         for name, got, ref in (("dq", gq[:, h], rq), ("dk", gk[:, h], rk), ("dv", gv[:, h], rv)):
             if heads is not None or h == 0:
                 _check(f"{tag} head {h} {name}", gradient_ok(got, ref))
@@ -123,26 +123,71 @@ def test_attention_backward_ragged_lengths(L):
     _compare_attention(f"L={L}", q, k, v, (dq, dk, dv), do_bits)
 
 
-def test_attention_backward_very_negative_scores():
+@pytest.mark.parametrize("scale", [SCALE, math.log(2.0)], ids=["scale_1_over_sqrt128", "scale_ln2"])
+def test_attention_backward_very_negative_scores(scale):
     """Query rows whose every score is far below zero (log-sum-exp near -100),
     with keys past L in the last tile (L = 200): the weight those absent keys
     would get, exp(-lse), overflows fp32, so the dq kernel must keep it out of
     dQ.  The keys share a direction u, but each also has a random part as large
     (nearly equal keys would make dQ = scale sum_j dS_j k_j cancel down to the
-    bf16 rounding of dS for any kernel)."""
+    bf16 rounding of dS for any kernel).  At scale ln 2 (scale log2(e) = 1, the
+    scale-folded layout) the dK/dV kernel starts its score chains from the
+    rows' -lse log2(e), which is -inf on the padded rows."""
     L, H = 200, 1
     rng = np.random.default_rng(77)
     u = 1.0 + 0.05 * rng.standard_normal(128)
     k_f = (u[None, :] + rng.standard_normal((L, 128)))[:, None, :]
     q_f = rng.standard_normal((L, H, 128))
-    q_f[::7] = -12.0 * u  # every 7th query row: scores between about -165 and -100
+    q_f[::7] = -12.0 * (SCALE / scale) * u  # every 7th query row: scores between about -165 and -100
     q = dev_bf16(wl.bf16_bits(q_f.astype(np.float32)))
     k = dev_bf16(wl.bf16_bits(k_f.astype(np.float32)))
     v = dev_bf16(_bf16_normal((L, H, 128), 78))
-    dq, dk, dv, do_bits = _attention_case(q, k, v, 79)
+    dq, dk, dv, do_bits = _attention_case(q, k, v, 79, scale=scale)
     for t in (dq, dk, dv):
         assert bool(torch.isfinite(t.float()).all())
-    _compare_attention("very negative scores", q, k, v, (dq, dk, dv), do_bits)
+    _compare_attention("very negative scores", q, k, v, (dq, dk, dv), do_bits, scale=scale)
+
+
+@pytest.mark.parametrize("idx", (0, 1, 2))
+def test_attention_backward_unit_scale_full(inputs, idx):
+    """The scale-folded layout's backward (q' = c q, scale ln 2, so scale log2(e)
+    is exactly 1 in fp32): the dK/dV kernel's unit-scale form, every head against
+    the oracle at scale ln 2."""
+    inp = inputs(idx)
+    q, k, v, gq, gk, pos = dev_inputs(inp)
+    h3attn_qk_prologue_scaled(q, k, gq, gk, pos, Q_SCALE)
+    dq, dk, dv, do_bits = _attention_case(q, k, v, 700 + idx, scale=math.log(2.0))
+    _compare_attention(f"unit scale workload {idx}", q, k, v, (dq, dk, dv), do_bits, scale=math.log(2.0))
+
+
+@pytest.mark.parametrize("L", [2, 63, 65, 130, 257, 600])
+def test_attention_backward_unit_scale_ragged(L):
+    H = 2
+    q = dev_bf16(_bf16_normal((L, H, 128), 110 + L))
+    k = dev_bf16(_bf16_normal((L, H, 128), 120 + L))
+    v = dev_bf16(_bf16_normal((L, H, 128), 130 + L))
+    dq, dk, dv, do_bits = _attention_case(q, k, v, 140 + L, scale=math.log(2.0) / 8)
+    # scale ln 2 / 8 leaves scale log2(e) at 1/8, the general form; ln 2 the unit form
+    _compare_attention(f"L={L} scale ln2/8", q, k, v, (dq, dk, dv), do_bits, scale=math.log(2.0) / 8)
+    qs = dev_bf16(wl.bf16_bits((host_f64(q) / 8).astype(np.float32)))
+    dq, dk, dv, do_bits = _attention_case(qs, k, v, 140 + L, scale=math.log(2.0))
+    _compare_attention(f"L={L} scale ln2", qs, k, v, (dq, dk, dv), do_bits, scale=math.log(2.0))
+
+
+@pytest.mark.parametrize("scale", [math.log(2.0) / 8, math.log(2.0)], ids=["general", "unit"])
+def test_attention_backward_single_token(scale):
+    """L = 1: the one weight is 1, so dV = dO and dQ = dK = 0 exactly; dS = P (dP -
+    delta) is then the fp32 difference of two evaluations of <dO, V> (one on the
+    matrix core, one in the vector units), a rounding-level value, so dK and dQ are
+    held to an absolute bound instead of the gradient gate's relative one."""
+    H = 3
+    q = dev_bf16(_bf16_normal((1, H, 128), 150))
+    k = dev_bf16(_bf16_normal((1, H, 128), 151))
+    v = dev_bf16(_bf16_normal((1, H, 128), 152))
+    dq, dk, dv, do_bits = _attention_case(q, k, v, 153, scale=scale)
+    assert np.array_equal(host_f64(dv), _as_f64(do_bits))
+    for t in (dq, dk):
+        assert float(np.abs(host_f64(t)).max()) <= 2.0 ** -14
 
 
 def _compare_attention_pooled(tag, q, k, v, grads, do_bits, heads):
