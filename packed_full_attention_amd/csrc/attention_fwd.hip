@@ -176,7 +176,9 @@ struct TileDma {
 __device__ __forceinline__ TileDma tile_dma(const char* tile_base, int64_t valid_bytes, uint32_t lds_tile,
                                             int wave) {
   const uint64_t b = (uint64_t)(uintptr_t)tile_base;
-  const uint32_t n = valid_bytes > 0xffffffffLL ? 0xffffffffu : (uint32_t)valid_bytes;
+  // valid_bytes > 0 here; past 2^32 - 1 the record count saturates (a 32-bit
+  // test of the high word: there is no 64-bit scalar less-than).
+  const uint32_t n = (uint32_t)((uint64_t)valid_bytes >> 32) != 0u ? 0xffffffffu : (uint32_t)valid_bytes;
   TileDma t;
   t.rsrc = i32x4_t{(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
                    (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)),
@@ -207,6 +209,11 @@ struct State {
   f32x16_t minit;  // log2 variant: -m in every slot, the score chain's start
   float m;         // exponent offset (raw score units; log2 variant: log2 units)
   float l;         // this lane-half's partial sum of P
+  // The K tile this iteration's DMA fetches (tile t + kStages, clamped to the
+  // last): its first byte and the valid bytes from there, advanced by one tile
+  // per iteration instead of recomputed from t (a 64-bit product per tile).
+  const char* kt_base;
+  int64_t kt_valid;
 };
 
 // LDS read addresses.  With the swizzle above, the k-step of a K read and the
@@ -462,8 +469,12 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
                                           bf16x8_t (&p_cur)[4], int t) {
   static_assert(!kFp8 || (kLog2 && kVT), "the FP8 score product is built on the log2 kernel");
   asm volatile("" : "+v"(a.k), "+v"(a.v0), "+v"(a.v1));
-  const TileDma kd = dma_k<kFp8>(x, t + kStages, ring(t));
-  const TileDma vd = dma_v<kVT>(x, t + kStages - 2, kVRing + ring(t + kStages - 2));
+  // The tile descriptors (scalar arithmetic) are made in the slot of their
+  // first piece, where the scalar unit works under that slot's matrix
+  // instruction, not all at the start of the iteration.
+  const auto k_desc = [&]() { return tile_dma(st.kt_base, st.kt_valid, x.lds_base + ring(t), x.wave); };
+  const auto v_desc = [&]() { return dma_v<kVT>(x, t + kStages - 2, kVRing + ring(t + kStages - 2)); };
+  TileDma kd, vd;
   const Addr b = at_buffers(a, ring(t + 1), kVRing + ring(t + kStages - 1));
 
   const float c = x.c, mc = st.m * c;
@@ -496,8 +507,14 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int sl = 0; sl < 20; ++sl) {
-      if (sl == 2) dma_piece(kd, x.kdma, 0);
-      if (sl == 8) dma_piece(vd, x.vdma, 0);
+      if (sl == 2) {
+        kd = k_desc();
+        dma_piece(kd, x.kdma, 0);
+      }
+      if (sl == 8) {
+        vd = v_desc();
+        dma_piece(vd, x.vdma, 0);
+      }
       if (sl == 14) dma_piece(vd, x.vdma, 1);
       if (sl + 2 < 20) load_op(sl + 2);
       if (sl % 5 == 0) {
@@ -538,9 +555,15 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
       // This iteration's DMA, one piece every 8 slots: issued all at once by
       // all 8 waves, the loads back up in the address unit and hold the waves
       // at the start of the iteration.
-      if (k == 4) dma_piece(kd, x.kdma, 0);
+      if (k == 4) {
+        kd = k_desc();
+        dma_piece(kd, x.kdma, 0);
+      }
       if (k == 12) dma_piece(kd, x.kdma, 1);
-      if (k == 20) dma_piece(vd, x.vdma, 0);
+      if (k == 20) {
+        vd = v_desc();
+        dma_piece(vd, x.vdma, 0);
+      }
       if (k == 28) dma_piece(vd, x.vdma, 1);
       if (k < 32) {
         if (k + 2 < 32) op[k + 2] = slot_operand<kVT>(k + 2, x.lds, b);
@@ -571,6 +594,8 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     store_pairs(w, p_cur);
     psum = sum4[0];
   } else {
+    kd = k_desc();
+    vd = v_desc();
     dma_k_all<kFp8>(kd, x.kdma);
     dma_all(vd, x.vdma);
     if (kFp8) {
@@ -597,6 +622,10 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
   }
   dma_wait_all_but<(kStages - 2) * dma_per_iteration<kFp8>()>();  // the last two iterations' DMA may be in flight
   __syncthreads();  // K(t+2), V(t) landed; every wave is done with K(t+1), V(t-1)
+  if (t + kStages + 1 < x.n_tiles) {
+    st.kt_base += x.ktile_bytes;
+    st.kt_valid -= x.ktile_bytes;
+  }
 }
 
 // A wave none of whose 32 query rows exists (only in the last, partial q-tile
@@ -850,6 +879,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   __syncthreads();
 
   // S(t) and P(t) live in s/p[t % 2]; odd/even pairs keep that choice static.
+  {
+    const int kt = kStages < x.n_tiles ? kStages : x.n_tiles - 1;
+    st.kt_base = x.kbase + kt * x.ktile_bytes;
+    st.kt_valid = (int64_t)(x.L - 1 - kt * kBN) * x.krow_bytes + (kFp8 ? kD : kD * 2);
+  }
   iteration<false, kLog2, kVT, kFp8>(x, st, a, s0, s1, p1, p0, 0);
   int t = 1;
   for (; t + 1 < x.n_tiles; t += 2) {
