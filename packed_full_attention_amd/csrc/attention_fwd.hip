@@ -214,6 +214,8 @@ struct State {
   // per iteration instead of recomputed from t (a 64-bit product per tile).
   const char* kt_base;
   int64_t kt_valid;
+  const char* vt_base;  // the same for the V (or V^T) tile, tile t + kStages - 2
+  int64_t vt_valid;
 };
 
 // LDS read addresses.  With the swizzle above, the k-step of a K read and the
@@ -473,7 +475,9 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
   // first piece, where the scalar unit works under that slot's matrix
   // instruction, not all at the start of the iteration.
   const auto k_desc = [&]() { return tile_dma(st.kt_base, st.kt_valid, x.lds_base + ring(t), x.wave); };
-  const auto v_desc = [&]() { return dma_v<kVT>(x, t + kStages - 2, kVRing + ring(t + kStages - 2)); };
+  const auto v_desc = [&]() {
+    return tile_dma(st.vt_base, st.vt_valid, x.lds_base + kVRing + ring(t + kStages - 2), x.wave);
+  };
   TileDma kd, vd;
   const Addr b = at_buffers(a, ring(t + 1), kVRing + ring(t + kStages - 1));
 
@@ -611,6 +615,11 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     }
     psum = kLog2 ? weights(s_cur, 1.f, 0.f, p_cur) : weights(s_cur, c, mc, p_cur);
   }
+  // The barrier first: the row-sum test below waits on the last row-sum
+  // instruction, and that wait then overlaps the barrier's.  What follows
+  // touches registers only.
+  dma_wait_all_but<(kStages - 2) * dma_per_iteration<kFp8>()>();  // the last two iterations' DMA may be in flight
+  __syncthreads();  // K(t+2), V(t) landed; every wave is done with K(t+1), V(t-1)
   if (__builtin_amdgcn_ballot_w64(!(psum <= kSumBound)) != 0) {
     cold_path();
     psum = kLog2 ? rebase_log2(s_cur, s_next, st, p_cur) : rebase(s_cur, st, c, p_cur);
@@ -620,11 +629,13 @@ __device__ __forceinline__ void iteration(const Ctx& x, State& st, Addr& a, cons
     cold_path();
     mask_tail<kVT>(s_next, (t + 1) * kBN, x.L, x.g);
   }
-  dma_wait_all_but<(kStages - 2) * dma_per_iteration<kFp8>()>();  // the last two iterations' DMA may be in flight
-  __syncthreads();  // K(t+2), V(t) landed; every wave is done with K(t+1), V(t-1)
   if (t + kStages + 1 < x.n_tiles) {
     st.kt_base += x.ktile_bytes;
     st.kt_valid -= x.ktile_bytes;
+  }
+  if (t + kStages - 1 < x.n_tiles) {
+    st.vt_base += kVT ? kBN * 2 : x.tile_bytes;
+    if (!kVT) st.vt_valid -= x.tile_bytes;
   }
 }
 
@@ -883,6 +894,9 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     const int kt = kStages < x.n_tiles ? kStages : x.n_tiles - 1;
     st.kt_base = x.kbase + kt * x.ktile_bytes;
     st.kt_valid = (int64_t)(x.L - 1 - kt * kBN) * x.krow_bytes + (kFp8 ? kD : kD * 2);
+    const int vt = kStages - 2 < x.n_tiles ? kStages - 2 : x.n_tiles - 1;
+    st.vt_base = x.vbase + (kVT ? (int64_t)vt * kBN * 2 : vt * x.tile_bytes);
+    st.vt_valid = kVT ? x.vt_valid : (int64_t)(x.L - 1 - vt * kBN) * x.row_bytes + kD * 2;
   }
   iteration<false, kLog2, kVT, kFp8>(x, st, a, s0, s1, p1, p0, 0);
   int t = 1;
