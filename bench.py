@@ -80,10 +80,16 @@ def kv_prologue_fp8_bytes(L: int, H: int) -> float:
 
 
 def kernel_source_sha() -> str:
-    """Hash of the forward attention kernel's sources (the file and the shared header)."""
+    """Hash of the forward attention kernel's code (the file and the shared header),
+    with comments and blank lines left out, so that a change of the text around the
+    code does not disown counters taken on the same code."""
     h = hashlib.sha256()
     for name in ("attention_fwd.hip", "gfx950_tile.h"):
-        h.update(open(os.path.join(ROOT, "packed_full_attention_amd", "csrc", name), "rb").read())
+        src = open(os.path.join(ROOT, "packed_full_attention_amd", "csrc", name)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        code = "\n".join(line.strip() for line in src.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

@@ -5,15 +5,21 @@
 // and unmasked over one packed document"; section 5 item h3_full_attention):
 //   out[i,h,:] = sum_j softmax_j(scale * <q[i,h,:], k[j,h,:]>) v[j,h,:]
 //
-// Two variants of one kernel.  The plain one computes exactly that, with the
-// scale applied in fp32 to each score.  The log2 one expects q to carry
+// One kernel template, four instantiations.  The plain one computes exactly
+// that, with the scale applied in fp32 to each score.  The log2 one expects q to carry
 // scale * log2(e) already (the Q/K prologue applies it in fp32 before q's
 // single rounding to bf16, so q is rounded once either way) and computes
 //   out[i,h,:] = sum_j 2^<q[i,h,:], k[j,h,:]> v[j,h,:] / sum_j 2^<q[i,h,:], k[j,h,:]>
 // which is the same softmax: its scores come out of the matrix cores in the
 // exponent's units, and the offset is subtracted there too (the score MFMA
 // chain starts from -m instead of 0), so no vector instruction stands between
-// a score and its exponential.
+// a score and its exponential.  Two more forms build on the log2 one: the Q
+// prologue form takes the raw q and applies Q's RMSNorm and MM-RoPE (with
+// gamma_q, the rotation table K's prologue wrote and the factor scale log2(e))
+// at its Q load, with the standalone prologue's fp32 operations and rounding;
+// the quantized-score form, on top of that, computes the scores from e4m3
+// operands (4 q' in registers, K' / 4 as bytes from its own K prologue) on the
+// FP8 matrix instruction, a cast its entry point declares.
 //
 // Numerical contract (same RFC, section 4): fp32 accumulation on the matrix
 // cores, one fixed key order (tile 0, 1, 2, ...), no split over keys, no
@@ -56,7 +62,8 @@
 // the waves read K(t+1) and V(t-1) while DMA (buffer_load_dwordx4 ... lds, no
 // VGPR staging) fills K(t+4) and V(t+2), each into the slot its ring freed in
 // iteration t-1; one barrier per tile, and a DMA has about two iterations to
-// land.  The DMA is issued by inline asm and awaited explicitly (vmcnt) before
+// land.  The tile descriptors advance by one tile per iteration.  The DMA is
+// issued by inline asm and awaited explicitly (vmcnt) before
 // each tile barrier: the compiler, which cannot prove that the in-flight writes
 // miss the buffers being read, would otherwise wait for them before every LDS
 // read.  Row-major tiles (one 256-byte row per key, sixteen 16-byte chunks)
