@@ -244,11 +244,14 @@ def main() -> int:
     plain = [lambda i: h3attn_qk_prologue(qs[i], ks[i], gq, gk, pos),
              lambda i: h3attn_forward(qs[i], ks[i], v, out, scale=scale)]
 
+    # The step the headline measures runs first, right after its warm-up, so the
+    # other paths' runs (which heat the chip and lower its power-limited clock)
+    # do not stand in front of it.
     refresh()
     for i in range(W):
-        for f in plain:
+        for f in fused:
             f(i)
-    plain_ms, (plain_pro, plain_att), _ = timed(plain, K, W)
+    ms_step, (t_kv, t_att), wall_ms = timed(fused, K, W)
     refresh()
     for i in range(W):
         for f in fast:
@@ -256,9 +259,9 @@ def main() -> int:
     fast_ms, (t_pro, t_vt_fast, t_att_fast), _ = timed(fast, K, W)
     refresh()
     for i in range(W):
-        for f in fused:
+        for f in plain:
             f(i)
-    ms_step, (t_kv, t_att), wall_ms = timed(fused, K, W)
+    plain_ms, (plain_pro, plain_att), _ = timed(plain, K, W)
     del qs, ks
 
     # The quantized-score variant reads q and k without writing them: no copies.
