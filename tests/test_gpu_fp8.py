@@ -183,3 +183,75 @@ def test_fp8_deterministic():
     a = run_fp8(inp)[0]
     b = run_fp8(inp)[0]
     assert np.array_equal(a, b)
+
+
+def test_fp8_head_subset_bit_identical():
+    """Heads are independent: heads 7..13 of the 56-head run of workload 1 equal an
+    H = 7 run on those heads alone, bit for bit (k8 and the output)."""
+    inp = wl.make_inputs(1)
+    out_full, k8_full, _, _, _ = run_fp8(inp)
+    sub = wl.Inputs(inp.workload, np.ascontiguousarray(inp.q[:, 7:14]), np.ascontiguousarray(inp.k[:, 7:14]),
+                    np.ascontiguousarray(inp.v[:, 7:14]), inp.gamma_q, inp.gamma_k, inp.pos, inp.stress_rows)
+    out_sub, k8_sub, _, _, _ = run_fp8(sub)
+    assert np.array_equal(out_sub, out_full[:, 7:14])
+    assert np.array_equal(k8_sub, k8_full[:, 7:14])
+
+
+@pytest.mark.parametrize("factor", [0.5, 2.0])
+def test_fp8_other_q_scales(factor):
+    """The cast takes 4 q' with q' = q_scale prologue(q) for any q_scale, not only
+    the softmax's scale log2(e)."""
+    inp = wl.make_inputs(0)
+    qs = float(np.float32(Q_SCALE * factor))
+    q, k, v, gq, gk, pos = dev_inputs(inp)
+    cs, k8, vt = h3attn_kv_prologue_fp8(k, v, gk, pos)
+    out = host_f64(h3attn_forward_fp8_qprologue(q, k8, vt, gq, cs, qs))
+    ref = oracle.packed_attention_fp8(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), inp.gamma_q, inp.gamma_k,
+                                      inp.pos, qs)
+    ok, e = attention_ok(out, ref)
+    print(f"q_scale x {factor}: {e}")
+    assert ok, e
+
+
+@pytest.mark.parametrize("alpha", [3.0, 8.0])
+def test_fp8_dominant_keys_and_rebase(alpha):
+    """Every position 0 (the rotation is the identity), query row i a copy of key
+    row j(i) and gamma_q = alpha gamma_k: key j(i)'s score exceeds the others by
+    about alpha 16 log2 units, so the output is nearly v[j(i)] and the exponent
+    offset must move mid-row; at alpha 8 a tile's weights reach 2^128 and must
+    lead to a rebase, not to inf or NaN.  Against the quantized-score oracle."""
+    L, H = 700, 2
+    rng = np.random.default_rng(91)
+    base = wl.random_document(L, H, seed=92)
+    j = rng.integers(0, L, size=L)
+    q_bits = np.ascontiguousarray(base.k[j])
+    gk = base.gamma_k
+    gq = wl.round_to_bf16((alpha * gk.astype(np.float64)).astype(np.float32))
+    pos = np.zeros((L, 3), dtype=np.int32)
+    inp = wl.Inputs(base.workload, q_bits, base.k, base.v, gq, gk, pos, base.stress_rows)
+    out, _, _, _, _ = run_fp8(inp)
+    ref = oracle.packed_attention_fp8(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), gq, gk, pos, Q_SCALE)
+    assert np.all(np.isfinite(out))
+    ok, e = attention_ok(out, ref)
+    print(f"alpha {alpha}: {e}")
+    assert ok, e
+
+
+def test_fp8_long_single_head():
+    """L = 70001 tokens of one head (1094 key tiles, L mod 256 = 113, L mod 64 = 49,
+    positions up to 5000): sampled rows against the quantized-score oracle, and
+    every k8 code checked."""
+    L, H = 70001, 1
+    inp = wl.random_document(L, H, seed=7101, pos_max=5000)
+    print(f"long single head FP8: L={L} H={H}", flush=True)
+    out, k8, _, _, _ = run_fp8(inp)
+    kr = oracle.mm_rope(oracle.rms_norm(inp.as_f64("k"), inp.gamma_k), inp.pos)
+    check_k8_codes("long single head k8", k8, kr)
+    rng = np.random.default_rng(7102)
+    rows = np.unique(np.concatenate([[0, 1, L - 50, L - 49, L - 2, L - 1], rng.choice(L, 40, replace=False)]))
+    qr = oracle.mm_rope(oracle.rms_norm(inp.as_f64("q")[rows], inp.gamma_q), inp.pos[rows])
+    q8, k8v = oracle.quantized_operands(qr[:, 0], kr[:, 0], Q_SCALE)
+    ref = oracle.quantized_attention_head(q8, k8v, inp.as_f64("v")[:, 0])
+    ok, e = attention_ok(out[rows, 0], ref)
+    print(f"long single head FP8 ({len(rows)} rows): {e}")
+    assert ok, e
