@@ -123,6 +123,22 @@ def measured_mfma(L: int, H: int):
     return float(busy.group(1)), (float(clk.group(1)) if clk else None)
 
 
+def clock_power(samples, n_launches: int, att_tflops: float) -> dict:
+    """Median socket power and shader clock over the sustained-load samples, and the
+    attention kernel's roofline fraction against the peak scaled to that clock."""
+    import statistics
+    busy = [(p, c) for p, c in samples if p > 500]
+    res = {"source": "amd-smi metric -p -c during a ~3 s run of the attention kernel after the timed region",
+           "launches": n_launches, "samples": len(busy), "socket_power_w_median": None, "sclk_mhz_median": None,
+           "roofline_frac_at_measured_clock": None}
+    if busy:
+        clk = statistics.median(c for _, c in busy)
+        res["socket_power_w_median"] = statistics.median(p for p, _ in busy)
+        res["sclk_mhz_median"] = clk
+        res["roofline_frac_at_measured_clock"] = round(att_tflops / (PEAK_BF16_TFLOPS * clk / 2400.0), 4)
+    return res
+
+
 def cpu_baseline(inp, L: int, H: int, budget_s: float = 12.0) -> dict:
     """The fp64 oracle, as it stands, on whole heads of the same workload."""
     import numpy as np
@@ -151,6 +167,60 @@ def cpu_baseline(inp, L: int, H: int, budget_s: float = 12.0) -> dict:
                       f"of {H}, all {L} query rows, {dt:.1f} s; host has {len(os.sched_getaffinity(0))} cores"}
 
 
+class ClockSampler:
+    """GPU clock and socket power, sampled by `amd-smi metric -p -c` in a child shell
+    started before this process touches the GPU; it idles until go() and stops at
+    stop().  Samples are taken only around a sustained run of the attention kernel
+    after the timed region, never during it."""
+
+    def __init__(self):
+        import subprocess
+        import tempfile
+        self.dir = tempfile.mkdtemp(prefix="h3attn_bench_")
+        script = (f'd="{self.dir}"; command -v amd-smi >/dev/null || exit 0; '
+                  'while [ ! -e "$d/stop" ]; do '
+                  'if [ -e "$d/go" ]; then echo "T $(date +%s.%N)" >> "$d/smi.txt"; '
+                  'timeout 5 amd-smi metric -p -c >> "$d/smi.txt" 2>&1; '
+                  'else sleep 0.05; fi; done')
+        try:
+            self.proc = subprocess.Popen(["bash", "-c", script], stdout=subprocess.DEVNULL,
+                                         stderr=subprocess.DEVNULL)
+        except OSError:
+            self.proc = None
+
+    def _touch(self, name):
+        open(os.path.join(self.dir, name), "w").close()
+
+    def go(self):
+        self._touch("go")
+
+    def stop(self):
+        """Ends the sampler; returns [(socket power W, max GFX clock MHz)] per sample."""
+        import shutil
+        import subprocess
+        try:
+            os.remove(os.path.join(self.dir, "go"))
+        except OSError:
+            pass
+        self._touch("stop")
+        if self.proc is not None:
+            try:
+                self.proc.wait(timeout=15)
+            except subprocess.TimeoutExpired:
+                self.proc.kill()
+                self.proc.wait()
+        samples = []
+        path = os.path.join(self.dir, "smi.txt")
+        if os.path.exists(path):
+            for block in open(path).read().split("\nT ")[1:]:
+                pw = re.search(r"SOCKET_POWER:\s*(\d+)", block)
+                ck = re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)", block)
+                if pw and ck:
+                    samples.append((int(pw.group(1)), max(int(c) for c in ck)))
+        shutil.rmtree(self.dir, ignore_errors=True)
+        return samples
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +236,8 @@ def main() -> int:
               "the path shards by heads with no exchange, so run one process per GPU on its head share.",
               file=sys.stderr)
         return 2
+
+    sampler = ClockSampler()  # before the GPU is touched: the child shell is not a fork of a GPU process
 
     import numpy as np
     import torch
@@ -252,6 +324,17 @@ def main() -> int:
         for f in fused:
             f(i)
     ms_step, (t_kv, t_att), wall_ms = timed(fused, K, W)
+    # Clock and power under sustained load: the attention kernel (which reads its
+    # inputs only) on the first step's inputs for about 3 s, sampled meanwhile.
+    sampler.go()
+    t_end = time.perf_counter() + 3.0
+    n_sustained = 0
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            h3attn_forward_log2_qprologue(qs[0], ks[0], vt, gq, rope_cs, q_scale, out)
+        torch.cuda.synchronize()
+        n_sustained += 20
+    clock_samples = sampler.stop()
     refresh()
     for i in range(W):
         for f in fast:
@@ -383,6 +466,7 @@ def main() -> int:
                      "flop_count": "2.5 x forward (dV, dP, dQ, dK, S)",
                      "prologue_backward_us": round(t_pbwd * 1e3, 2),
                      "prologue_backward_gbs": round(pbwd_bytes / (t_pbwd * 1e-3) / 1e9, 1)},
+        "clock_power": clock_power(clock_samples, n_sustained, att_tflops),
         "wall_ms_timed_region": round(wall_ms, 2),
     }
     if not args.no_cpu_baseline:
