@@ -28,8 +28,10 @@ sample, timed on this host's cores.  The roofline's `traffic`,
 `mfma_busy_pct` and `sclk_mhz` are not measured by this run: they are read
 from the committed counter summaries under profiles/ (named in
 `counters_from`) and given only while those were taken on the current kernel
-source.  Inputs are generated, copied to the GPU and resident in
-HBM before the timed region starts.
+code; `clock_power` is measured by this run (amd-smi samples of socket power
+and shader clock during a ~3 s run of the attention kernel after the timed
+region).  Inputs are generated, copied to the GPU and resident in HBM before
+the timed region starts; the headline step is timed first.
 """
 from __future__ import annotations
 
