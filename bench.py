@@ -211,16 +211,22 @@ class ClockSampler:
             except subprocess.TimeoutExpired:
                 self.proc.kill()
                 self.proc.wait()
-        samples = []
         path = os.path.join(self.dir, "smi.txt")
-        if os.path.exists(path):
-            for block in open(path).read().split("\nT ")[1:]:
-                pw = re.search(r"SOCKET_POWER:\s*(\d+)", block)
-                ck = re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)", block)
-                if pw and ck:
-                    samples.append((int(pw.group(1)), max(int(c) for c in ck)))
+        samples = parse_smi(open(path).read()) if os.path.exists(path) else []
         shutil.rmtree(self.dir, ignore_errors=True)
         return samples
+
+
+def parse_smi(text: str):
+    """[(socket power W, highest GFX clock MHz)] from `amd-smi metric -p -c` outputs,
+    each preceded by a line "T <time>"."""
+    samples = []
+    for block in ("\n" + text).split("\nT ")[1:]:
+        pw = re.search(r"SOCKET_POWER:\s*(\d+)", block)
+        ck = re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)", block)
+        if pw and ck:
+            samples.append((int(pw.group(1)), max(int(c) for c in ck)))
+    return samples
 
 
 def main() -> int:

@@ -12,3 +12,17 @@ def test_more_than_one_gpu_is_refused():
                          text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_power_clock_sample_parsing():
+    """The amd-smi text bench.py samples: socket power and the highest GFX clock per
+    sample; samples without both are skipped."""
+    import bench
+    block = ("T 1.5\nGPU: 0\n    POWER:\n        SOCKET_POWER: {p} W\n    CLOCK:\n"
+             "        GFX_0:\n            CLK: {a} MHz\n            MIN_CLK: 500 MHz\n"
+             "        GFX_1:\n            CLK: {b} MHz\n")
+    text = block.format(p=1320, a=1850, b=1875) + block.format(p=1335, a=1901, b=1890) + "T 2.0\nerror\n"
+    assert bench.parse_smi(text) == [(1320, 1875), (1335, 1901)]
+    res = bench.clock_power(bench.parse_smi(text) + [(300, 2400)], 100, 1250.0)
+    assert res["samples"] == 2 and res["sclk_mhz_median"] == 1888.0 and res["socket_power_w_median"] == 1327.5
+    assert abs(res["roofline_frac_at_measured_clock"] - 1250.0 / (bench.PEAK_BF16_TFLOPS * 1888.0 / 2400.0)) < 1e-4
