@@ -205,6 +205,13 @@ __device__ __forceinline__ void block_tile(int b, int H, int n_full, int& head, 
 // (t, 0) starts the DMA of tile t + 2 into the slot of tile t - 2 and ends
 // with the tile's one barrier.
 //
+// The dP^T chain starts from -delta instead of 0, so it leaves the matrix
+// core as dP - delta and dS is one multiplication; when c = scale log2(e) is
+// exactly 1 (the scale-folded layout's scale ln 2), the S^T chain likewise
+// starts from -lse log2(e) - 1, and the weight is one exponential with no FMA
+// in front of it.  Both starts are one value per lane (its query row),
+// written into the accumulators at the top of each step.
+//
 // The weights are computed halved, P/2 = exp2(c S - lse log2 e - 1) with the
 // exponential's output clamped to [0, 1] (a free instruction modifier), and dQ
 // is scaled by 2 scale at the end: every true weight is at most 1 (up to the
@@ -233,16 +240,24 @@ constexpr int kDqSteps = dq_slot(15) + 4 > 24 ? dq_slot(15) + 4 : 24;
 // slot pk (half kbp; kPrev: there is one).  s_c, dp_c: this block's S^T and
 // dP^T; s_n, dp_n: the next block's; ds_p: the previous block's dS^T / 2
 // operand, ds_c: this block's.  nl = -lse log2(e) - 1, dl = delta of the
-// lane's query row.
-template <bool kPrev, typename Dma>
+// lane's query row; kUnit: c == 1, the S^T chain starts from nl.
+template <bool kPrev, bool kUnit, typename Dma>
 __device__ __forceinline__ void dq_step(const lds_char* nk, const lds_char* nv, int kbn, const lds_char* pk, int kbp,
                                         const Addr& a, float c, float nl, float dl, const f32x16_t& s_c,
                                         const f32x16_t& dp_c, f32x16_t& s_n, f32x16_t& dp_n,
                                         const bf16x8_t (&ds_p)[2], bf16x8_t (&ds_c)[2], f32x16_t (&acc)[4],
                                         const bf16x8_t (&qop)[8], const bf16x8_t (&dop)[8], const Dma& dma) {
   constexpr int kAheadDq = 2;
-  s_n = f32x16_t{};
-  dp_n = f32x16_t{};
+  // The chains' start values, made opaque here so that the compiler builds
+  // them in the accumulators each step instead of holding a broadcast copy of
+  // each (32 registers) through the loop.
+  float nls = nl, ndl = -dl;
+  asm volatile("" : "+v"(nls), "+v"(ndl));
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    s_n[e] = kUnit ? nls : 0.f;
+    dp_n[e] = ndl;
+  }
   bf16x8_t op[24];
 #pragma unroll
   for (int j = 0; j < kAheadDq; ++j)
@@ -269,9 +284,9 @@ __device__ __forceinline__ void dq_step(const lds_char* nk, const lds_char* nv, 
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      if (k == dq_slot(e)) xa[e] = fmaf(s_c[e], c, nl);
+      if (k == dq_slot(e)) xa[e] = kUnit ? s_c[e] : fmaf(s_c[e], c, nl);
       if (k == dq_slot(e) + 1) p[e] = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(xa[e]), 0.f, 1.f);
-      if (k == dq_slot(e) + 2) x[e] = p[e] * (dp_c[e] - dl);
+      if (k == dq_slot(e) + 2) x[e] = p[e] * dp_c[e];
     }
 #pragma unroll
     for (int m = 0; m < 8; ++m)
@@ -283,6 +298,7 @@ __device__ __forceinline__ void dq_step(const lds_char* nk, const lds_char* nv, 
     ds_c[h] = __builtin_bit_cast(bf16x8_t, u32x4_t{pair[4 * h], pair[4 * h + 1], pair[4 * h + 2], pair[4 * h + 3]});
 }
 
+template <bool kUnit>
 __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ out, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
@@ -365,7 +381,12 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
   }
 
   // Block (0, 0)'s scores.
-  f32x16_t sa = f32x16_t{}, da = f32x16_t{};
+  f32x16_t sa, da;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    sa[e] = kUnit ? nl : 0.f;
+    da[e] = -dl;
+  }
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     sa = mfma32(row_operand(kslot(0), 0, ks, a), qop[ks], sa);
@@ -380,17 +401,17 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
     const auto dma = [&](int ks) {
       if (ks % kEvery == 1 && ks < 24) piece(2, ks / kEvery);
     };
-    dq_step<false>(kslot(0), vslot(0), 1, kslot(0), 0, a, c, nl, dl, sa, da, sb, db, dsb, dsa, acc, qop, dop, dma);
+    dq_step<false, kUnit>(kslot(0), vslot(0), 1, kslot(0), 0, a, c, nl, dl, sa, da, sb, db, dsb, dsa, acc, qop, dop, dma);
     dma_wait_all_but<kDqPieces>();  // tile 1 landed; tile 2 may be in flight
     __syncthreads();
   }
   for (int t = 0; t < n_tiles; ++t) {
-    dq_step<true>(kslot(t + 1), vslot(t + 1), 0, kslot(t), 0, a, c, nl, dl, sb, db, sa, da, dsa, dsb, acc, qop, dop,
+    dq_step<true, kUnit>(kslot(t + 1), vslot(t + 1), 0, kslot(t), 0, a, c, nl, dl, sb, db, sa, da, dsa, dsb, acc, qop, dop,
                   no_dma);
     const auto dma = [&](int ks) {
       if (ks % kEvery == 1 && ks < 24) piece(t + 3, ks / kEvery);
     };
-    dq_step<true>(kslot(t + 1), vslot(t + 1), 1, kslot(t), 1, a, c, nl, dl, sa, da, sb, db, dsb, dsa, acc, qop, dop,
+    dq_step<true, kUnit>(kslot(t + 1), vslot(t + 1), 1, kslot(t), 1, a, c, nl, dl, sa, da, sb, db, dsb, dsa, acc, qop, dop,
                   dma);
     dma_wait_all_but<kDqPieces>();
     __syncthreads();
@@ -681,8 +702,12 @@ hipError_t launch_attention_backward(const uint16_t* q, const uint16_t* k, const
   const int n_full = (int)(L / kRows);
   const int Lp = (int)((L + kTile - 1) / kTile * kTile);
   const float c = scale * kLog2e;
-  hipLaunchKernelGGL(attention_bwd_dq_kernel, grid, block, 0, stream, q, k, v, out, dout, lse, dq, stats, (int)L,
-                     (int)H, Lp, c, scale, n_full);
+  if (c == 1.0f)
+    hipLaunchKernelGGL(attention_bwd_dq_kernel<true>, grid, block, 0, stream, q, k, v, out, dout, lse, dq, stats,
+                       (int)L, (int)H, Lp, c, scale, n_full);
+  else
+    hipLaunchKernelGGL(attention_bwd_dq_kernel<false>, grid, block, 0, stream, q, k, v, out, dout, lse, dq, stats,
+                       (int)L, (int)H, Lp, c, scale, n_full);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 fgrid((unsigned)(((L + kFusedRows - 1) / kFusedRows) * (int64_t)H));
