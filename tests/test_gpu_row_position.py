@@ -1,4 +1,4 @@
-"""GPU tests: a query row's result does not depend on where the launch puts it.
+"""GPU tests: a row's result does not depend on where the launch puts it.
 
 The "MiniMax-H3 WS1/WS2 kernel roadmap" RFC, section 4 ("Numerical contract",
 item 2), requires reduction and addition order to be independent of packed-row
@@ -10,8 +10,9 @@ rows (and what belongs to them: their rotation-table rows for the fused
 forms; their out, dout and log-sum-exp rows for dq) must therefore permute the
 output rows bit for bit.  The permutations move rows between full tiles, the
 partial tile and both halves of a tile.  dk and dv sum over the query rows, in
-row order, so for them a permutation changes only the summation order: they are
-held to the gradient gate instead.
+row order, so for them a permutation of the queries changes only the summation
+order: they are held to the gradient gate there, and tested bit for bit under a
+permutation of the key rows with the queries fixed.
 """
 import math
 
@@ -105,3 +106,29 @@ def test_backward_dq_rows_keep_their_bits(L, H, unit):
         for name, got, ref in (("dk", host_f64(dk2), ref_dk), ("dv", host_f64(dv2), ref_dv)):
             ok, e = gradient_ok(got, ref)
             assert ok, (name, e)
+
+
+@pytest.mark.parametrize("L,H", SHAPES)
+@pytest.mark.parametrize("unit", [False, True], ids=["scale", "unit_scale"])
+def test_backward_dk_dv_rows_keep_their_bits(L, H, unit):
+    # The key side: the dk/dv kernel gives each wave 32 keys and streams the
+    # queries in one order, so with q, out, dout and lse held fixed, permuting
+    # the key rows (k and v together) permutes dk and dv bit for bit.
+    inp = wl.random_document(L, H, seed=750 + L, pos_max=2000)
+    q, k, v, gq, gk, pos = dev_inputs(inp)
+    if unit:
+        h3attn_qk_prologue_scaled(q, k, gq, gk, pos, Q_SCALE)
+        scale = math.log(2.0)
+    else:
+        h3attn_qk_prologue(q, k, gq, gk, pos)
+        scale = SCALE
+    out, lse = h3attn_forward_lse(q, k, v, scale=scale)
+    dout = dev_bf16(wl.random_document(L, H, seed=760 + L).q)
+    _, dk, dv = h3attn_attention_backward(q, k, v, out, dout, lse, scale=scale)
+    ref_dk, ref_dv = host_bits(dk), host_bits(dv)
+    for i, perm in enumerate(perms(L, L + 4)):
+        print(f"backward keys L={L} H={H} unit={unit} permutation {i}", flush=True)
+        _, dk2, dv2 = h3attn_attention_backward(q, take_rows(k, perm), take_rows(v, perm), out, dout, lse,
+                                                scale=scale)
+        assert np.array_equal(host_bits(dk2), ref_dk[perm])
+        assert np.array_equal(host_bits(dv2), ref_dv[perm])
