@@ -16,7 +16,7 @@ output follows its own declared definition and accuracy profile and so never
 enters `value`.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
-                    [--no-cpu-baseline] [--copy-probe]
+                    [--no-cpu-baseline] [--copy-probe] [--no-clock-sample]
 
 Prints one JSON line.  `value` is attention TFLOP/s (4 L^2 128 H per step)
 over the whole step's time; the `roofline` object prices the attention kernel
@@ -30,7 +30,10 @@ from the committed counter summaries under profiles/ (named in
 `counters_from`) and given only while those were taken on the current kernel
 code; `clock_power` is measured by this run (amd-smi samples of socket power
 and shader clock during a ~3 s run of the attention kernel after the timed
-region).  Inputs are generated, copied to the GPU and resident in HBM before
+region), except under a profiler or with --no-clock-sample: a profiler's
+preloaded library initialises the GPU in every child process, and the
+sampler's amd-smi (a script started through `env`) would then replace a GPU
+process by exec.  Inputs are generated, copied to the GPU and resident in HBM before
 the timed region starts; the headline step is timed first.
 """
 from __future__ import annotations
@@ -125,10 +128,19 @@ def measured_mfma(L: int, H: int):
     return float(busy.group(1)), (float(clk.group(1)) if clk else None)
 
 
-def clock_power(samples, n_launches: int, att_tflops: float) -> dict:
+def under_profiler() -> bool:
+    """True when rocprofv3 launched this process (it passes its settings to the
+    program through ROCPROF* environment variables)."""
+    return any(name.startswith("ROCPROF") for name in os.environ)
+
+
+def clock_power(samples, n_launches: int, att_tflops: float, skipped: str | None = None) -> dict:
     """Median socket power and shader clock over the sustained-load samples, and the
     attention kernel's roofline fraction against the peak scaled to that clock."""
     import statistics
+    if skipped is not None:
+        return {"source": None, "skipped": skipped, "launches": n_launches, "samples": 0,
+                "socket_power_w_median": None, "sclk_mhz_median": None, "roofline_frac_at_measured_clock": None}
     busy = [(p, c) for p, c in samples if p > 500]
     res = {"source": "amd-smi metric -p -c during a ~3 s run of the attention kernel after the timed region",
            "launches": n_launches, "samples": len(busy), "socket_power_w_median": None, "sclk_mhz_median": None,
@@ -238,6 +250,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one elementwise copy of a known size first (for counter scaling)")
+    ap.add_argument("--no-clock-sample", action="store_true",
+                    help="no amd-smi clock and power samples (always off under a profiler)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
@@ -245,7 +259,11 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    sampler = ClockSampler()  # before the GPU is touched: the child shell is not a fork of a GPU process
+    # The sampler starts before the GPU is touched (its shell is not a fork of a
+    # GPU process); under a profiler every child initialises the GPU, so none.
+    no_sample = ("--no-clock-sample" if args.no_clock_sample
+                 else "running under rocprofv3" if under_profiler() else None)
+    sampler = None if no_sample else ClockSampler()
 
     import numpy as np
     import torch
@@ -334,15 +352,16 @@ def main() -> int:
     ms_step, (t_kv, t_att), wall_ms = timed(fused, K, W)
     # Clock and power under sustained load: the attention kernel (which reads its
     # inputs only) on the first step's inputs for about 3 s, sampled meanwhile.
-    sampler.go()
-    t_end = time.perf_counter() + 3.0
+    if sampler is not None:
+        sampler.go()
+    t_end = time.perf_counter() + (3.0 if sampler is not None else 0.0)
     n_sustained = 0
     while time.perf_counter() < t_end:
         for _ in range(20):
             h3attn_forward_log2_qprologue(qs[0], ks[0], vt, gq, rope_cs, q_scale, out)
         torch.cuda.synchronize()
         n_sustained += 20
-    clock_samples = sampler.stop()
+    clock_samples = sampler.stop() if sampler is not None else []
     refresh()
     for i in range(W):
         for f in fast:
@@ -474,7 +493,7 @@ def main() -> int:
                      "flop_count": "2.5 x forward (dV, dP, dQ, dK, S)",
                      "prologue_backward_us": round(t_pbwd * 1e3, 2),
                      "prologue_backward_gbs": round(pbwd_bytes / (t_pbwd * 1e-3) / 1e9, 1)},
-        "clock_power": clock_power(clock_samples, n_sustained, att_tflops),
+        "clock_power": clock_power(clock_samples, n_sustained, att_tflops, no_sample),
         "wall_ms_timed_region": round(wall_ms, 2),
     }
     if not args.no_cpu_baseline:

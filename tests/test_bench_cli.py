@@ -26,3 +26,18 @@ def test_power_clock_sample_parsing():
     res = bench.clock_power(bench.parse_smi(text) + [(300, 2400)], 100, 1250.0)
     assert res["samples"] == 2 and res["sclk_mhz_median"] == 1888.0 and res["socket_power_w_median"] == 1327.5
     assert abs(res["roofline_frac_at_measured_clock"] - 1250.0 / (bench.PEAK_BF16_TFLOPS * 1888.0 / 2400.0)) < 1e-4
+
+
+def test_no_clock_sampler_under_a_profiler(monkeypatch):
+    """Under rocprofv3 (ROCPROF* variables in the environment) bench.py starts no
+    amd-smi sampler: the profiler's preloaded library would initialise the GPU in
+    the sampler's processes, which then replace themselves by exec."""
+    import bench
+    for name in [n for n in list(bench.os.environ) if n.startswith("ROCPROF")]:
+        monkeypatch.delenv(name)
+    assert not bench.under_profiler()
+    monkeypatch.setenv("ROCPROF_KERNEL_TRACE", "1")
+    assert bench.under_profiler()
+    res = bench.clock_power([(1320, 1875)], 0, 1250.0, "running under rocprofv3")
+    assert res["skipped"] == "running under rocprofv3" and res["samples"] == 0
+    assert res["sclk_mhz_median"] is None and res["roofline_frac_at_measured_clock"] is None
