@@ -26,14 +26,18 @@
  *     allocates nothing and only enqueues work on `stream` (0 = the null
  *     stream): the calls return before the GPU finishes, and the caller
  *     synchronises.  Between calls it keeps only the text of the calling
- *     thread's last error (h3attn_last_error, thread-local).
+ *     thread's last error (h3attn_last_error, thread-local) and, for
+ *     h3attn_attention_backward_noalloc alone, a device array per device
+ *     (its address, looked up once, and whatever the last such call left in
+ *     it).
  *   - Arguments are validated on the host before any launch; a rejected call
  *     launches nothing and leaves every buffer untouched.  There is no
  *     fallback path.  Device data is not inspected: non-finite inputs
  *     propagate, and positions must satisfy |pos| <= 2^24 (exact in fp32).
  *   - Results are deterministic: a fixed key order and one workgroup per
  *     output row, independent of launch geometry, so repeated calls are
- *     bit-identical.
+ *     bit-identical, and a query row's output (a key row's dk, dv) does not
+ *     depend on where in the launch the row falls.
  */
 #ifndef H3ATTN_H
 #define H3ATTN_H
