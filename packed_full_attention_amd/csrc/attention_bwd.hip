@@ -188,6 +188,30 @@ __device__ __forceinline__ void block_tile(int b, int H, int n_full, int& head, 
   }
 }
 
+// The dq kernel's blocks: as block_tile, except that the last n_half full
+// 256-row tiles (in head-major order) run as two workgroups of 128 rows each
+// (blocks H n_full - n_half .. H n_full + n_half - 1), whose waves 0..3 own
+// the rows; those workgroups finish sooner and fill a last round that would
+// otherwise leave CUs idle.  active: the waves that own rows.
+__device__ __forceinline__ void dq_tile(int b, int H, int n_full, int n_half, int& head, int& row0, int& active) {
+  const int nfb = H * n_full;
+  active = kWaves;
+  if (b < nfb - n_half) {
+    const int nwhole = nfb - n_half, xcd = b & 7, slot = b >> 3, per = nwhole >> 3, rem = nwhole & 7;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
+    head = logical / n_full;
+    row0 = (logical - head * n_full) * kRows;
+  } else if (b < nfb + n_half) {
+    const int j = b - (nfb - n_half), logical = nfb - n_half + (j >> 1);
+    head = logical / n_full;
+    row0 = (logical - head * n_full) * kRows + (j & 1) * (kRows / 2);
+    active = kWaves / 2;
+  } else {
+    head = b - nfb - n_half;
+    row0 = n_full * kRows;
+  }
+}
+
 // ---------------------------------------------------------------- dq (+ delta)
 // Software-pipelined over 32-key blocks, like the dk/dv kernel below but at
 // two waves per SIMD: block (t, kb) is the kb-th half of key tile t, and the
@@ -302,10 +326,11 @@ template <bool kUnit>
 __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ out, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
-    uint16_t* __restrict__ dq, float* __restrict__ stats, int L, int H, int Lp, float c, float scale, int n_full) {
+    uint16_t* __restrict__ dq, float* __restrict__ stats, int L, int H, int Lp, float c, float scale, int n_full,
+    int n_half) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kDqStages * kTileBytes];  // K ring, then V ring
-  int head, qtile;
-  block_tile(blockIdx.x, H, n_full, head, qtile);
+  int head, row0, active;
+  dq_tile(blockIdx.x, H, n_full, n_half, head, row0, active);
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t tok_stride = (int64_t)H * kD;
@@ -333,15 +358,17 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
 #pragma unroll
     for (int j = 0; j < kDqPieces; ++j) piece(t, j);
 
-  const int row = qtile * kRows + wave * 32 + col;
-  const bool valid = row < L;
+  const bool owner = wave < active;  // this wave's rows belong to this workgroup
+  const int row = row0 + wave * 32 + col;
+  const bool valid = owner && row < L;
+  const int lrow = owner ? row : L;  // rows past L load as zeros
   bf16x8_t qop[8], dop[8];
-  load_row_operands(q + (int64_t)head * kD, tok_stride, row, L, g, qop);
-  load_row_operands(dout + (int64_t)head * kD, tok_stride, row, L, g, dop);
+  load_row_operands(q + (int64_t)head * kD, tok_stride, lrow, L, g, qop);
+  load_row_operands(dout + (int64_t)head * kD, tok_stride, lrow, L, g, dop);
   float dsum = 0.f;  // delta = <dO, O> over this lane's 64 channels, then both halves
   {
     bf16x8_t oop[8];
-    load_row_operands(out + (int64_t)head * kD, tok_stride, row, L, g, oop);
+    load_row_operands(out + (int64_t)head * kD, tok_stride, lrow, L, g, oop);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
@@ -349,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
   }
   const float dl = pair_sum(dsum);
   const float lse2 = valid ? lse[(int64_t)head * L + row] * kLog2e : 0.f;
-  if (g == 0 && row < Lp) {  // statistics for the dk/dv kernel; rows L .. Lp-1 get weight 0 there
+  if (owner && g == 0 && row < Lp) {  // statistics for the dk/dv kernel; rows L .. Lp-1 get weight 0 there
     stats[(int64_t)head * Lp + row] = valid ? -lse2 : -INFINITY;
     stats[((int64_t)H + head) * Lp + row] = valid ? -dl : 0.f;
   }
@@ -362,10 +389,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_bwd_dq_kernel(
   dma_wait();
   __syncthreads();
 
-  // A wave none of whose rows exists (only in a head's last, partial query
-  // tile) carries its share of the ring DMA and takes part in every barrier,
-  // computing nothing: its SIMD's matrix core is left to the other wave.
-  if (qtile * kRows + wave * 32 >= L) {
+  // A wave none of whose rows exists (in a head's last, partial query tile)
+  // or that owns none (waves 4..7 of a half tile) carries its share of the
+  // ring DMA and takes part in every barrier, computing nothing: its SIMD's
+  // matrix core is left to the other wave.
+  if (!owner || row0 + wave * 32 >= L) {
 #pragma unroll
     for (int j = 0; j < kDqPieces; ++j) piece(2, j);
     dma_wait_all_but<kDqPieces>();
@@ -654,7 +682,11 @@ __global__ __launch_bounds__(64 * kFusedWaves, 1) void attention_bwd_dkdv_kernel
 
 }  // namespace
 
-int64_t backward_grid_blocks(int64_t L, int32_t H) { return ((L + kRows - 1) / kRows) * (int64_t)H; }
+// An upper bound (for validation): every q-tile, plus up to 1024 run as two halves.
+int64_t backward_grid_blocks(int64_t L, int32_t H) {
+  const int64_t nfull = (L / kRows) * H;
+  return ((L + kRows - 1) / kRows) * (int64_t)H + (nfull < 1024 ? nfull : 1024);
+}
 int64_t backward_workspace_bytes(int64_t L, int32_t H) { return 2 * (int64_t)H * ((L + kTile - 1) / kTile * kTile) * 4; }
 int backward_block_threads() { return kThreads; }
 // One past the last byte a row-tile DMA reads, from the tile's first byte (row
@@ -698,16 +730,17 @@ hipError_t launch_attention_backward(const uint16_t* q, const uint16_t* k, const
                                      const uint16_t* out, const uint16_t* dout, const float* lse,
                                      uint16_t* dq, uint16_t* dk, uint16_t* dv, float* stats, int64_t L,
                                      int32_t H, float scale, hipStream_t stream) {
-  const dim3 grid((unsigned)backward_grid_blocks(L, H)), block(kThreads);
+  const int n_half = forward_half_tiles(L, H);  // the same 256-row tiles, one workgroup per CU
+  const dim3 grid((unsigned)(((L + kRows - 1) / kRows) * (int64_t)H + n_half)), block(kThreads);
   const int n_full = (int)(L / kRows);
   const int Lp = (int)((L + kTile - 1) / kTile * kTile);
   const float c = scale * kLog2e;
   if (c == 1.0f)
     hipLaunchKernelGGL(attention_bwd_dq_kernel<true>, grid, block, 0, stream, q, k, v, out, dout, lse, dq, stats,
-                       (int)L, (int)H, Lp, c, scale, n_full);
+                       (int)L, (int)H, Lp, c, scale, n_full, n_half);
   else
     hipLaunchKernelGGL(attention_bwd_dq_kernel<false>, grid, block, 0, stream, q, k, v, out, dout, lse, dq, stats,
-                       (int)L, (int)H, Lp, c, scale, n_full);
+                       (int)L, (int)H, Lp, c, scale, n_full, n_half);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 fgrid((unsigned)(((L + kFusedRows - 1) / kFusedRows) * (int64_t)H));

@@ -91,6 +91,8 @@
 // dispatched last, and its waves that own no query row only carry their share
 // of the DMA, so those shorter workgroups fill the grid's final round.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <float.h>
 #include <stdint.h>
 
@@ -760,7 +762,7 @@ template <bool kLog2, bool kVT, bool kQPro, bool kFp8 = false>
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, float* __restrict__ lse, int L, int H, int Lp, float scale_log2e, int n_qfull,
-    const float* __restrict__ gamma_q, const float* __restrict__ rope_cs, float q_scale) {
+    const float* __restrict__ gamma_q, const float* __restrict__ rope_cs, float q_scale, int n_half) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStages * kTileBytes];
 
   // Blocks are dispatched in increasing order, round-robin over the 8 XCDs
@@ -769,18 +771,31 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   // them: the workgroups that share one head's K/V then share one L2.  The
   // last H blocks, dispatched last, take each head's partial q-tile (if L is
   // not a multiple of 256), which finish sooner (see stream_only) and so fill
-  // the final round of the grid.
-  const int b = blockIdx.x, nfb = H * n_qfull;
-  int head, qtile;
-  if (b < nfb) {
+  // the final round of the grid.  When that round would also hold full
+  // q-tiles on otherwise idle CUs, the last n_half full tiles (in head-major
+  // order) run instead as two workgroups of 128 rows each, blocks
+  // H * n_qfull - n_half .. H * n_qfull + n_half - 1: waves 0..3 own the rows,
+  // one per SIMD, and waves 4..7 only stream K/V, so the round ends sooner.  A
+  // wave computes its rows the same way in any of these workgroups.
+  const int b = blockIdx.x, nfb = H * n_qfull, nwhole = nfb - n_half;
+  int head, qtile, row0, active_waves = kWaves;
+  if (b < nwhole) {
     const int xcd = b & 7, slot = b >> 3;
-    const int per = nfb >> 3, rem = nfb & 7;
+    const int per = nwhole >> 3, rem = nwhole & 7;
     const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
     head = logical / n_qfull;
     qtile = logical - head * n_qfull;
+    row0 = qtile * kBM;
+  } else if (b < nfb + n_half) {
+    const int j = b - nwhole, logical = nwhole + (j >> 1);
+    head = logical / n_qfull;
+    qtile = logical - head * n_qfull;
+    row0 = qtile * kBM + (j & 1) * (kBM / 2);
+    active_waves = kWaves / 2;
   } else {
-    head = b - nfb;
+    head = b - nfb - n_half;
     qtile = n_qfull;
+    row0 = qtile * kBM;
   }
 
   const int tid = threadIdx.x;
@@ -831,14 +846,14 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
 #pragma unroll
   for (int i = 0; i < kStages - 2; ++i) dma_all(dma_v<kVT>(x, i, kVRing + ring(i)), x.vdma);
 
-  if (qtile * kBM + x.wave * 32 >= L) {
+  if (x.wave >= active_waves || row0 + x.wave * 32 >= L) {
     stream_only<kVT, kFp8>(x);
     return;
   }
 
   // Q^T operand: lane holds Q[row][16ks + 8g .. +7] for its query row.
   State st;
-  const int qrow = qtile * kBM + x.wave * 32 + col;
+  const int qrow = row0 + x.wave * 32 + col;
   if (qrow < L) {
     const uint16_t* p = q + (int64_t)qrow * tok_stride + (int64_t)head * kD + 8 * x.g;
 #pragma unroll
@@ -944,7 +959,45 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
 
 }  // namespace
 
-int64_t attention_grid_blocks(int64_t L, int32_t H) { return ((L + kBM - 1) / kBM) * (int64_t)H; }
+// Compute units of the current device (the launch's round size), looked up
+// once per device; 256 (MI355X) if the query fails.
+static int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// How many of the last full q-tiles run as two 128-row workgroups.  With one
+// workgroup per CU, the grid runs in rounds of `cus` workgroups; when its last
+// round holds full tiles and there is room to run each of them as two half
+// tiles, it does (the half tiles finish sooner: one wave per SIMD, half the
+// rows); otherwise none.  The result bits do not depend on this choice.
+int forward_half_tiles(int64_t L, int32_t H) {
+  const int64_t nfull = (L / kBM) * H, npart = (L % kBM) ? H : 0;
+  const int64_t cus = device_cu_count();
+  const int64_t last = (nfull + npart) % cus;  // workgroups in the last round
+  const int64_t flast = last - npart;          // the full tiles among them
+  if (last == 0 || flast <= 0 || last + flast > cus || flast > 1024) return 0;
+  return (int)flast;
+}
+
+// Workgroups of a forward launch: every q-tile, plus one per tile run as two
+// halves; the bound attention_grid_blocks (used by validation, which makes no
+// HIP call) allows for up to 1024 of those.
+static dim3 forward_grid(int64_t L, int32_t H, int n_half) {
+  return dim3((unsigned)(((L + kBM - 1) / kBM) * (int64_t)H + n_half));
+}
+int64_t attention_grid_blocks(int64_t L, int32_t H) {
+  const int64_t nfull = (L / kBM) * H;
+  return ((L + kBM - 1) / kBM) * (int64_t)H + (nfull < 1024 ? nfull : 1024);
+}
 int attention_block_threads() { return kThreads; }
 
 // One past the last byte, counted from the tile's first byte, that a tile DMA
@@ -960,13 +1013,14 @@ hipError_t launch_attention_forward(const uint16_t* q, const uint16_t* k, const 
                                     uint16_t* out, float* lse, int64_t L, int32_t H, float scale, bool log2,
                                     hipStream_t stream) {
   const int n_qfull = (int)(L / kBM);  // full 256-row q-tiles per head
-  const dim3 grid((unsigned)attention_grid_blocks(L, H));
+  const int n_half = forward_half_tiles(L, H);
+  const dim3 grid = forward_grid(L, H, n_half);
   if (log2)  // v is V^T
     hipLaunchKernelGGL((attention_fwd_kernel<true, true, false>), grid, dim3(kThreads), 0, stream, q, k, v, out,
-                       lse, (int)L, (int)H, (int)vt_padded_length(L), 1.0f, n_qfull, nullptr, nullptr, 1.0f);
+                       lse, (int)L, (int)H, (int)vt_padded_length(L), 1.0f, n_qfull, nullptr, nullptr, 1.0f, n_half);
   else
     hipLaunchKernelGGL((attention_fwd_kernel<false, false, false>), grid, dim3(kThreads), 0, stream, q, k, v, out,
-                       lse, (int)L, (int)H, 0, scale * kLog2e, n_qfull, nullptr, nullptr, 1.0f);
+                       lse, (int)L, (int)H, 0, scale * kLog2e, n_qfull, nullptr, nullptr, 1.0f, n_half);
   return hipGetLastError();
 }
 
@@ -974,9 +1028,10 @@ hipError_t launch_attention_forward_fp8(const uint16_t* q_raw, const uint8_t* k8
                                         const float* gamma_q, const float* rope_cs, int64_t L, int32_t H,
                                         float q_scale, hipStream_t stream) {
   const int n_qfull = (int)(L / kBM);
-  hipLaunchKernelGGL((attention_fwd_kernel<true, true, true, true>), dim3((unsigned)attention_grid_blocks(L, H)),
-                     dim3(kThreads), 0, stream, q_raw, reinterpret_cast<const uint16_t*>(k8), vt, out, nullptr,
-                     (int)L, (int)H, (int)vt_padded_length(L), 1.0f, n_qfull, gamma_q, rope_cs, q_scale);
+  const int n_half = forward_half_tiles(L, H);
+  hipLaunchKernelGGL((attention_fwd_kernel<true, true, true, true>), forward_grid(L, H, n_half), dim3(kThreads), 0,
+                     stream, q_raw, reinterpret_cast<const uint16_t*>(k8), vt, out, nullptr, (int)L, (int)H,
+                     (int)vt_padded_length(L), 1.0f, n_qfull, gamma_q, rope_cs, q_scale, n_half);
   return hipGetLastError();
 }
 
@@ -984,9 +1039,10 @@ hipError_t launch_attention_forward_qprologue(const uint16_t* q_raw, const uint1
                                               uint16_t* out, const float* gamma_q, const float* rope_cs,
                                               int64_t L, int32_t H, float q_scale, hipStream_t stream) {
   const int n_qfull = (int)(L / kBM);
-  hipLaunchKernelGGL((attention_fwd_kernel<true, true, true>), dim3((unsigned)attention_grid_blocks(L, H)),
-                     dim3(kThreads), 0, stream, q_raw, k, vt, out, nullptr, (int)L, (int)H,
-                     (int)vt_padded_length(L), 1.0f, n_qfull, gamma_q, rope_cs, q_scale);
+  const int n_half = forward_half_tiles(L, H);
+  hipLaunchKernelGGL((attention_fwd_kernel<true, true, true>), forward_grid(L, H, n_half), dim3(kThreads), 0, stream,
+                     q_raw, k, vt, out, nullptr, (int)L, (int)H, (int)vt_padded_length(L), 1.0f, n_qfull, gamma_q,
+                     rope_cs, q_scale, n_half);
   return hipGetLastError();
 }
 

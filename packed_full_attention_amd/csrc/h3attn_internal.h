@@ -93,9 +93,14 @@ int64_t vt_bytes(int64_t L, int32_t H);
 int64_t transpose_grid_blocks(int64_t L, int32_t H);
 int transpose_block_threads();
 
-// Grid size (workgroups) and workgroup size (threads) of the forward launch
-// for (L, H), and the prologue's grid size; used by validation.
+// An upper bound on the grid size (workgroups) of a forward launch for (L, H),
+// its workgroup size (threads), and the prologue's grid size; used by
+// validation (no HIP call).
 int64_t attention_grid_blocks(int64_t L, int32_t H);
+// How many of the last full 256-row q-tiles a forward or dq launch runs as two
+// 128-row workgroups (to fill the grid's last round); results do not depend
+// on it.
+int forward_half_tiles(int64_t L, int32_t H);
 int attention_block_threads();
 int64_t prologue_grid_blocks(int64_t L);
 
