@@ -33,7 +33,10 @@ Q_SCALE = float(np.float32(SCALE * math.log2(math.e)))
 
 # (L, H): a partial tile of 88 rows after two full ones; one of 232 rows; a
 # single row past one full tile; several heads with a partial tile of 100 rows.
-SHAPES = [(600, 3), (1000, 2), (257, 1), (1380, 5)]
+# In those the grid is one sparse round, so every full tile runs as two
+# 128-row halves; at L = 35890, H = 2 it holds 282 tiles, and 256 run whole, 24
+# as halves and 2 as partial tiles, so rows move between all three kinds.
+SHAPES = [(600, 3), (1000, 2), (257, 1), (1380, 5), (35890, 2)]
 
 
 def perms(L: int, seed: int):
@@ -69,7 +72,7 @@ def test_fused_forward_rows_keep_their_bits(L, H):
         assert np.array_equal(got, ref[perm])
 
 
-@pytest.mark.parametrize("L,H", SHAPES[:2])
+@pytest.mark.parametrize("L,H", SHAPES[:2] + SHAPES[-1:])
 def test_quantized_score_forward_rows_keep_their_bits(L, H):
     inp = wl.random_document(L, H, seed=720 + L, pos_max=2000)
     q, k, v, gq, gk, pos = dev_inputs(inp)
